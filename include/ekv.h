@@ -1,0 +1,191 @@
+/*
+ * ekv.h -- C ABI of libekv: support-aware sparse alpha-entmax decode over a
+ * paged, GQA-shared KV cache on AMD MI355X (gfx950).
+ *
+ * Method: "EntmaxKV: Support-Aware Decoding for Entmax Attention" (Duarte,
+ * Couceiro, Treviso; arXiv 2605.21649), below [EKV].  One decode step for a
+ * batch of single-token queries is
+ *
+ *     ekv_score_pages  ->  ekv_select  ->  ekv_entmax_decode
+ *
+ * on page statistics that ekv_build_page_stats writes once per page (at
+ * prefill, or when a page fills).  [EKV] section 4.1 is the pipeline,
+ * section 4.2 the page scoring, section 4.3 the two selection policies,
+ * section 4.4 the hand-off of selected page indices (and the threshold
+ * estimate) from selection to decode without a host round trip.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every pointer argument other than `shape`, `workspace_bytes` and the
+ *    returned strings is a DEVICE pointer on the current HIP device.  The
+ *    library never allocates, frees, copies to or from the host, or
+ *    synchronises; every kernel is enqueued on `stream` (a hipStream_t passed
+ *    as void*, NULL = the legacy default stream).  The caller owns all memory.
+ *  - Argument checks run on the host before anything is enqueued; a failed
+ *    check returns an error code and leaves every buffer untouched.
+ *    ekv_last_error() then returns a message (thread-local).
+ *  - Launch failures return EKV_ERR_HIP.  Outputs are undefined after any
+ *    error.
+ *  - Non-finite inputs are not detected; they propagate.
+ *  - Calls on one stream may be enqueued back to back; the library is
+ *    stateless and reentrant.  Calls that share a workspace buffer must be
+ *    ordered (same stream, or synchronised by the caller).
+ *  - Workspace: an entry point that takes `workspace` reports the bytes it
+ *    needs in *workspace_bytes and returns EKV_OK without enqueuing anything
+ *    when `workspace` is NULL; when `workspace` is not NULL, *workspace_bytes
+ *    must hold its size and a size below the need returns EKV_ERR_WORKSPACE.
+ *    The workspace must be 256-byte aligned.
+ *
+ * Layout (row-major, innermost index last)
+ * -----------------------------------------
+ *   B = batch, HQ = num_q_heads, G = num_kv_groups, r = HQ/G, D = head_dim,
+ *   P = page_size, MP = max_pages_per_seq, NP = num_phys_pages.
+ *   q           [B][HQ][D]          kv_dtype
+ *   k_cache     [NP][G][P][D]       kv_dtype   (one page-group tile contiguous)
+ *   v_cache     [NP][G][P][D]       kv_dtype
+ *   page_table  [B][MP]             int32, logical page -> physical page
+ *   seq_lens    [B]                 int32, tokens of each sequence (0..MP*P)
+ *   kmin, kmax  [NP][G][D]          kv_dtype   (exact per-channel min / max)
+ *   kmean, kvar [NP][G][D]          stat_dtype (per-channel mean / variance)
+ * Sequence b has M_b = ceil(seq_lens[b]/P) logical pages; logical page p holds
+ * tokens [pP, min((p+1)P, seq_lens[b])).  Query head h reads group
+ * floor(h / r) (consecutive heads share a group).  Slots of a last page beyond
+ * the sequence end are never read.
+ */
+#ifndef EKV_H
+#define EKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EKV_OK = 0,
+    EKV_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent shape, bad value */
+    EKV_ERR_UNSUPPORTED = 2,   /* valid request outside what is built        */
+    EKV_ERR_WORKSPACE = 3,     /* workspace smaller than reported need       */
+    EKV_ERR_HIP = 4            /* a HIP launch or runtime call failed        */
+} ekv_status;
+
+typedef enum { EKV_F32 = 0, EKV_BF16 = 1 } ekv_dtype;
+
+typedef enum {
+    EKV_SEL_TOPK = 0,   /* [EKV] section 4.3 "Top-k page selection"            */
+    EKV_SEL_GAUSS = 1   /* [EKV] section 4.3 "Gaussian-aware entmax selection"  */
+} ekv_selector;
+
+/* Problem shape.  Supported: D in {64, 128}; P == 16; r in {1, 2, 4, 8};
+ * G <= 16; kv_dtype in {EKV_F32, EKV_BF16}; stat_dtype in {EKV_F32, EKV_BF16}. */
+typedef struct {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_groups;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_pages_per_seq;
+    int32_t num_phys_pages;
+    int32_t kv_dtype;     /* ekv_dtype of q, k_cache, v_cache, kmin, kmax */
+    int32_t stat_dtype;   /* ekv_dtype of kmean, kvar                      */
+} ekv_shape;
+
+/* Page key statistics ([EKV] section 4.2 and Appendix B.1 for the per-channel
+ * min/max; mean and variance are the page statistics the Gaussian selector of
+ * section 4.3 reads).  For each listed logical page of each sequence, over
+ * the page's valid tokens only, per group and channel:
+ *   kmin/kmax = exact min/max of the stored keys (same dtype, bit-exact),
+ *   kmean     = (1/n_p) sum k,   kvar = (1/n_p) sum (k - kmean)^2
+ *               (fp32 accumulation in token order; rounded to stat_dtype).
+ * Results are written at the page's PHYSICAL index.
+ *   page_list : NULL = every logical page of every sequence; otherwise n_list
+ *               device entries b*MP + p (entries with p >= M_b are skipped).
+ *   kmin,kmax : may both be NULL (not written); kmean,kvar likewise; not all
+ *               four NULL.
+ * Not on the per-step path: run at prefill or when a page fills.          */
+ekv_status ekv_build_page_stats(const ekv_shape* shape, const void* k_cache,
+                                const int32_t* page_table, const int32_t* seq_lens,
+                                const int32_t* page_list, int32_t n_list,
+                                void* kmin, void* kmax, void* kmean, void* kvar,
+                                void* stream);
+
+/* Query-aware page scores ([EKV] section 4.2 and Appendix B.1; section 4.3).
+ * EKV_SEL_TOPK (reads kmin, kmax; writes score [B][G][MP] fp32):
+ *   u_{h,p} = (1/sqrt(D)) sum_i max(q_{h,i} kmax_{p,i}, q_{h,i} kmin_{p,i}),
+ *   score_{g,p} = max over the r heads of group g of u_{h,p}.
+ * EKV_SEL_GAUSS (reads kmean, kvar; writes mu, sigma [B][HQ][MP] fp32):
+ *   mu_{h,p} = (1/sqrt(D)) sum_i q_{h,i} kmean_{p,i},
+ *   sigma_{h,p} = sqrt((1/D) sum_i q_{h,i}^2 kvar_{p,i})
+ *   (per-head moments of the page's token scores, channels treated as
+ *   independent).
+ * Entries for p >= M_b are not written.  Accumulation is fp32.            */
+ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void* q,
+                           const int32_t* page_table, const int32_t* seq_lens,
+                           const void* kmin, const void* kmax,
+                           const void* kmean, const void* kvar,
+                           float* score, float* mu, float* sigma, void* stream);
+
+/* Candidate page selection, one page set per (sequence, KV group)
+ * ([EKV] section 4.3).
+ * EKV_SEL_TOPK: the min(budget_pages, M_b) pages with the largest score;
+ *   ties go to the lower logical page index.  `alpha`, `z`, mu, sigma unused.
+ * EKV_SEL_GAUSS: per head, tau_hat solves the distributional threshold
+ *   equation ([EKV] Appendix C.2, Eq. (18))
+ *       sum_p n_p E[[(alpha-1) S_p - tau_hat]_+^beta] = 1,
+ *       S_p ~ N(mu_{h,p}, sigma_{h,p}^2), beta = 1/(alpha-1),
+ *   with the closed-form truncated-normal expectations (alpha in
+ *   {2, 3/2, 4/3}; other alpha -> EKV_ERR_UNSUPPORTED).  Page p of group g is
+ *   a candidate when max_h (mu_{h,p} - tau_hat_h/(alpha-1)) / sigma_{h,p} >= -z
+ *   (the page rule of Eq. (21) is not legible on the page; this is the reading
+ *   this library takes); candidates are ranked by that margin (ties to the
+ *   lower index) and at most budget_pages are kept; at least one page is kept.
+ * Outputs: sel_pages [B][G][budget_pages] int32 logical indices in ascending
+ *   order, unused tail = -1; sel_count [B][G] int32; tau_hat [B][HQ] fp32
+ *   (GAUSS only; may be NULL).  Needs a workspace (see conventions).       */
+ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* seq_lens,
+                      float alpha, int32_t budget_pages, float z,
+                      const float* score, const float* mu, const float* sigma,
+                      int32_t* sel_pages, int32_t* sel_count, float* tau_hat,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Exact alpha-entmax attention over the tokens of the selected pages
+ * ([EKV] section 4.1; alpha-entmax of section 2.2):
+ *   s_{h,j} = q_h . k_{g(h),j} / sqrt(D) for j in C_tok (valid tokens of the
+ *   group's selected pages), x = (alpha-1) s, beta = 1/(alpha-1),
+ *   tau_h from sum_j [x_j - tau_h]_+^beta = 1,
+ *   p_j = [x_j - tau_h]_+^beta (exact zeros), out_h = sum_j p_j v_{g(h),j}.
+ *   alpha == 1 is softmax over C_tok and tau is then the log-partition
+ *   log sum_j exp(s_j).  alpha > 1 may be any value; 1.5 and 2 use a closed
+ *   form on the support found.
+ * sel_pages == NULL selects every page (full-cache decode); otherwise
+ *   sel_pages [B][G][sel_stride] logical page indices (ascending not
+ *   required) and sel_count [B][G] of them are used.
+ * Outputs: out [B][HQ][D] fp32; tau [B][HQ] fp32 (x units; log-partition for
+ *   alpha == 1); support [B][HQ] int32 nonzero count (NULL ok);
+ *   delta [B][HQ] fp32 (NULL ok; needs tau_ref): dropped mass
+ *   1 - sum_{j in C_tok} p_ref_j of the distribution whose threshold is
+ *   tau_ref [B][HQ] (e.g. a full-cache decode's tau) ([EKV] section 3.1).
+ * An empty candidate set (seq_lens[b] == 0 or sel_count == 0) gives
+ *   out = 0, tau = -inf, support = 0, delta = 1.
+ * Needs a workspace (see conventions); its size depends on sel_pages being
+ * NULL or not and on sel_stride.                                           */
+ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* page_table, const int32_t* seq_lens,
+                             const int32_t* sel_pages, const int32_t* sel_count,
+                             int32_t sel_stride, float alpha, const float* tau_ref,
+                             float* out, float* tau, int32_t* support, float* delta,
+                             void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Message describing the last error returned on this thread ("" if none). */
+const char* ekv_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int32_t ekv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EKV_H */

@@ -1,0 +1,534 @@
+// Sparse alpha-entmax decode over the selected pages ("EntmaxKV:
+// Support-Aware Decoding for Entmax Attention", section 4.1; alpha-entmax of
+// section 2.2; dropped mass of section 3.1).
+//
+//   logits_kernel  grid (page chunks, B*G): gathers each selected page-group
+//                  K tile (16 tokens x D, contiguous) through the page table,
+//                  one token per 16-lane row, and writes s = q.k/sqrt(D) for
+//                  the group's r heads into a [B][HQ][slots] workspace
+//                  (invalid slots -inf).  Per chunk and head it also keeps
+//                  (max, sum exp(s - max), valid count).
+//   tau_kernel     grid (HQ, B): the threshold of sum [x - tau]_+^beta = 1,
+//                  x = (alpha-1) s.  Only x > max(x) - 1 can be in the
+//                  support (the top term alone is at most 1), so those
+//                  candidates are compacted into LDS in slot order; Newton
+//                  steps from tau = max(x) - 1 (where the sum is >= 1) rise
+//                  monotonically to the root because the sum is convex and
+//                  decreasing in tau (beta >= 1); for beta = 1 and 2 the
+//                  closed form on the support found then gives tau exactly
+//                  (beta = 2: tau = m - sqrt((1 - V)/k), m the mean and V the
+//                  centred sum of squares of the k support values).  alpha = 1
+//                  (softmax) takes the log-partition straight from the chunk
+//                  partials.
+//   pv_kernel      grid (slot chunks, B*G): p = [x - tau]_+^beta has exact
+//                  zeros, so only slots with p > 0 for some head of the group
+//                  are compacted and only their V rows are read; partial sums
+//                  need no rescaling.
+//   reduce_kernel  grid (HQ, B): fixed-order sum of the chunk partials.
+// No atomics: every result is bitwise reproducible.
+#include "ekv_device.h"
+#include "ekv_internal.h"
+
+namespace ekv {
+
+enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
+constexpr int kLogitUnroll = 4;
+constexpr int kCandCap = 8192;
+
+// -------------------------------------------------------------- logits ----
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void logits_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int ppb,
+    int nslot, int nchunk1, float inv_sqrt_d, float* __restrict__ logits, float* __restrict__ part1) {
+    constexpr int CH = D / kRow;
+    constexpr int NW = Vec<T, CH>::NW;
+    __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
+    const int unit = blockIdx.y;
+    const int b = unit / G, g = unit - b * G;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int i0 = blockIdx.x * ppb;
+    const int i1 = min(cnt, i0 + ppb);
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;          // token within the page
+
+    Vec<T, CH> qv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
+
+    const int hj = lane < R ? lane : 0;        // head owned by this lane (lanes < R)
+    float* lrow = logits + ((size_t)b * HQ + g * R + hj) * nslot;
+    float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+
+    for (int i = i0; i < i1; i += kLogitUnroll) {
+        Vec<T, CH> kv[kLogitUnroll];
+        int lp[kLogitUnroll];
+        bool ok[kLogitUnroll];
+#pragma unroll
+        for (int u = 0; u < kLogitUnroll; ++u) {
+            const int ii = i + u;
+            lp[u] = ii < i1 ? (sel ? sel[ii] : ii) : -1;
+            ok[u] = lp[u] >= 0 && lp[u] < M;
+            int phys = ok[u] ? page_table[(size_t)b * MP + lp[u]] : -1;
+            ok[u] = ok[u] && phys >= 0 && phys < NP;
+            if (ok[u]) kv[u].load(k_cache + (((size_t)phys * G + g) * kPage + row) * D + lane * CH);
+        }
+#pragma unroll
+        for (int u = 0; u < kLogitUnroll; ++u) {
+            const int ii = i + u;
+            if (ii >= i1) break;                       // block-uniform
+            float mine = -INFINITY;
+            if (ok[u]) {                               // block-uniform
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float acc = 0.0f;
+                    if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+                        for (int c = 0; c < CH; ++c) acc = fmaf(qv[j].get(c), kv[u].get(c), acc);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < NW; ++w)
+                            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv[u].w[w]),
+                                                                  __builtin_bit_cast(bf16x2_t, qv[j].w[w]),
+                                                                  acc, false);
+                    }
+                    acc = row_sum16(acc) * inv_sqrt_d;
+                    mine = (lane == j) ? acc : mine;
+                }
+                if (lp[u] * kPage + row >= n) mine = -INFINITY;   // past the sequence end
+            }
+            if (lane < R) {
+                lrow[(size_t)ii * kPage + row] = mine;
+                if (mine > -INFINITY) {
+                    if (mine > run_m) {
+                        run_l = run_l * expf(run_m - mine) + 1.0f;
+                        run_m = mine;
+                    } else {
+                        run_l += expf(mine - run_m);
+                    }
+                    run_c += 1.0f;
+                }
+            }
+        }
+    }
+    if (lane < R) {
+        sh_m[row][lane] = run_m;
+        sh_l[row][lane] = run_l;
+        sh_c[row][lane] = run_c;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        const int j = threadIdx.x;
+        float m = -INFINITY;
+        for (int r2 = 0; r2 < kRow; ++r2) m = fmaxf(m, sh_m[r2][j]);
+        float l = 0.0f, c = 0.0f;
+        for (int r2 = 0; r2 < kRow; ++r2) {
+            if (sh_m[r2][j] > -INFINITY) l += sh_l[r2][j] * expf(sh_m[r2][j] - m);
+            c += sh_c[r2][j];
+        }
+        float* o = part1 + (((size_t)b * HQ + g * R + j) * nchunk1 + blockIdx.x) * 3;
+        o[0] = m;
+        o[1] = l;
+        o[2] = c;
+    }
+}
+
+// ----------------------------------------------------------------- tau ----
+struct TauSums {
+    float s1, s0, k;
+};
+
+__device__ __forceinline__ float powb(float d, int mode, float beta) {
+    return mode == kModeBeta1 ? d : (mode == kModeBeta2 ? d * d : powf(d, beta));
+}
+
+__global__ __launch_bounds__(256) void tau_kernel(
+    const float* __restrict__ logits, const float* __restrict__ part1,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
+    int mode, float alpha, float beta, const float* __restrict__ tau_ref, float* __restrict__ tau_out,
+    int32_t* __restrict__ support_out, float* __restrict__ delta_out) {
+    __shared__ float cand[kCandCap];
+    __shared__ float red[8];
+    __shared__ int wsum[4];
+    int phase = 0;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int R = HQ / G;
+    const int unit = b * G + h / R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int nused = cnt * kPage;
+    const size_t oh = (size_t)b * HQ + h;
+
+    // Combine the chunk partials (fixed order).
+    const float* pm = part1 + oh * nchunk1 * 3;
+    float mx = -INFINITY;
+    for (int c = threadIdx.x; c < nchunk1; c += 256) mx = fmaxf(mx, pm[c * 3]);
+    mx = block_max<4>(mx, red, phase);
+    float L = 0.0f, C = 0.0f;
+    for (int c = threadIdx.x; c < nchunk1; c += 256) {
+        const float m = pm[c * 3];
+        if (m > -INFINITY) L += pm[c * 3 + 1] * expf(m - mx);
+        C += pm[c * 3 + 2];
+    }
+    L = block_sum<4>(L, red, phase);
+    C = block_sum<4>(C, red, phase);
+    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+    if (!(C > 0.0f)) {
+        if (threadIdx.x == 0) {
+            tau_out[oh] = -INFINITY;
+            if (support_out) support_out[oh] = 0;
+            if (delta_out) delta_out[oh] = 1.0f;
+        }
+        return;
+    }
+    if (mode == kModeSoftmax) {
+        const float lse = mx + logf(L);
+        float kept = 0.0f;
+        if (delta_out) {
+            for (int c = threadIdx.x; c < nchunk1; c += 256) {
+                const float m = pm[c * 3];
+                if (m > -INFINITY) kept += pm[c * 3 + 1] * expf(m - tref);
+            }
+            kept = block_sum<4>(kept, red, phase);
+        }
+        if (threadIdx.x == 0) {
+            tau_out[oh] = lse;
+            if (support_out) support_out[oh] = (int32_t)C;
+            if (delta_out) delta_out[oh] = 1.0f - kept;
+        }
+        return;
+    }
+
+    const float a = alpha - 1.0f;
+    const float lo = a * mx - 1.0f;
+    const float* lrow = logits + oh * nslot;
+
+    // Candidates x > max(x) - 1, compacted in slot order.
+    int ncand = 0;
+    for (int base = 0; base < nused; base += 256) {
+        const int sl = base + threadIdx.x;
+        const float x = sl < nused ? a * lrow[sl] : -INFINITY;
+        const bool f = x > lo;
+        const uint64_t m = __ballot(f);
+        const int wid = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) wsum[wid] = __popcll(m);
+        __syncthreads();
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            off += i < wid ? wsum[i] : 0;
+            tot += wsum[i];
+        }
+        const int pos = ncand + off + lanes_below(m);
+        if (f && pos < kCandCap) cand[pos] = x;
+        ncand += tot;
+        __syncthreads();
+    }
+    const bool in_lds = ncand <= kCandCap;
+
+    // Sums over the candidates (LDS), or over every slot with the same filter.
+    auto sums = [&](float t, float t_keep_above, bool want_s0) -> TauSums {
+        float s1 = 0.0f, s0 = 0.0f, k = 0.0f;
+        const int lim = in_lds ? ncand : nused;
+        for (int i = threadIdx.x; i < lim; i += 256) {
+            const float x = in_lds ? cand[i] : a * lrow[i];
+            const float dd = x - t;
+            if (x > t_keep_above && dd > 0.0f) {
+                s1 += powb(dd, mode, beta);
+                if (want_s0) s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? dd : powf(dd, beta - 1.0f));
+                k += 1.0f;
+            }
+        }
+        TauSums r;
+        r.s1 = block_sum<4>(s1, red, phase);
+        r.s0 = want_s0 ? block_sum<4>(s0, red, phase) : 0.0f;
+        r.k = block_sum<4>(k, red, phase);
+        return r;
+    };
+
+    float tau = lo;
+    if (beta >= 1.0f) {
+        for (int it = 0; it < 100; ++it) {
+            const TauSums r = sums(tau, lo, true);
+            const float F = r.s1 - 1.0f;
+            if (!(F > 0.0f) || !(r.s0 > 0.0f)) break;
+            const float nt = tau + F / (beta * r.s0);
+            if (!(nt > tau)) break;
+            tau = nt;
+        }
+    } else {
+        // beta < 1 (alpha > 2): the sum is not convex; bisect.
+        float hi = a * mx - powf(C, 1.0f - alpha);
+        float l2 = lo;
+        for (int it = 0; it < 60; ++it) {
+            const float mid = 0.5f * (l2 + hi);
+            const TauSums r = sums(mid, lo, false);
+            if (r.s1 - 1.0f >= 0.0f) l2 = mid; else hi = mid;
+        }
+        tau = 0.5f * (l2 + hi);
+    }
+
+    // Closed form on the support found (beta = 1 or 2), kept if consistent.
+    if (mode == kModeBeta1 || mode == kModeBeta2) {
+        float sx = 0.0f, k = 0.0f, mn = INFINITY, rest = -INFINITY;
+        const int lim = in_lds ? ncand : nused;
+        for (int i = threadIdx.x; i < lim; i += 256) {
+            const float x = in_lds ? cand[i] : a * lrow[i];
+            if (x > tau) { sx += x; k += 1.0f; mn = fminf(mn, x); }
+            else if (x > lo) rest = fmaxf(rest, x);
+        }
+        sx = block_sum<4>(sx, red, phase);
+        k = block_sum<4>(k, red, phase);
+        mn = -block_max<4>(-mn, red, phase);
+        rest = block_max<4>(rest, red, phase);
+        float tcf = NAN;
+        if (k > 0.0f) {
+            if (mode == kModeBeta1) {
+                tcf = (sx - 1.0f) / k;
+            } else {
+                const float mean = sx / k;
+                float v = 0.0f;
+                for (int i = threadIdx.x; i < lim; i += 256) {
+                    const float x = in_lds ? cand[i] : a * lrow[i];
+                    if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
+                }
+                v = block_sum<4>(v, red, phase);
+                if (v <= 1.0f) tcf = mean - sqrtf((1.0f - v) / k);
+            }
+        }
+        if (tcf == tcf && mn > tcf && !(rest > tcf)) tau = tcf;
+    }
+
+    // Support size and dropped mass with respect to tau_ref.
+    const TauSums fin = sums(tau, lo, false);
+    float kept = 0.0f;
+    if (delta_out) kept = sums(tref, lo, false).s1;
+    if (threadIdx.x == 0) {
+        tau_out[oh] = tau;
+        if (support_out) support_out[oh] = (int32_t)fin.k;
+        if (delta_out) delta_out[oh] = 1.0f - kept;
+    }
+}
+
+// ------------------------------------------------------------------ PV ----
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void pv_kernel(
+    const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
+    const float* __restrict__ tau, int G, int MP, int NP, int nslot, int spb, int nchunk3, int mode,
+    float alpha, float beta, float* __restrict__ part3) {
+    constexpr int CH = D / kRow;
+    __shared__ int list_slot[256];
+    __shared__ float list_p[256][R];
+    __shared__ int wsum[4];
+    __shared__ float wred[4][R][D];
+    const int unit = blockIdx.y;
+    const int b = unit / G, g = unit - b * G;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int nused = cnt * kPage;
+    const int s0 = blockIdx.x * spb;
+    const int s1 = min(nused, s0 + spb);
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    const float a = alpha - 1.0f;
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+
+    float tj[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) tj[j] = tau[(size_t)b * HQ + g * R + j];
+
+    float acc[R][CH];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[j][c] = 0.0f;
+
+    for (int base = s0; base < s1; base += 256) {
+        const int sl = base + threadIdx.x;
+        float pj[R];
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            float p = 0.0f;
+            if (sl < s1 && tj[j] > -INFINITY) {
+                const float s = logits[((size_t)b * HQ + g * R + j) * nslot + sl];
+                if (mode == kModeSoftmax) {
+                    p = s > -INFINITY ? expf(s - tj[j]) : 0.0f;
+                } else {
+                    const float dd = a * s - tj[j];
+                    p = dd > 0.0f ? powb(dd, mode, beta) : 0.0f;
+                }
+            }
+            pj[j] = p;
+            any = any || p > 0.0f;
+        }
+        const uint64_t m = __ballot(any);
+        const int wid = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) wsum[wid] = __popcll(m);
+        __syncthreads();
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            off += i < wid ? wsum[i] : 0;
+            tot += wsum[i];
+        }
+        if (any) {
+            const int pos = off + lanes_below(m);
+            list_slot[pos] = sl;
+#pragma unroll
+            for (int j = 0; j < R; ++j) list_p[pos][j] = pj[j];
+        }
+        __syncthreads();
+        for (int e = row; e < tot; e += kRow) {
+            const int slot = list_slot[e];
+            const int ip = slot >> 4, t = slot & (kPage - 1);
+            const int lp = sel ? sel[ip] : ip;
+            if (lp < 0 || lp >= M) continue;
+            const int phys = page_table[(size_t)b * MP + lp];
+            if (phys < 0 || phys >= NP) continue;
+            Vec<T, CH> vv;
+            vv.load(v_cache + (((size_t)phys * G + g) * kPage + t) * D + lane * CH);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float p = list_p[e][j];
+#pragma unroll
+                for (int c = 0; c < CH; ++c) acc[j][c] = fmaf(p, vv.get(c), acc[j][c]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // Reduce the 16 rows: rows of a wave by cross-lane adds (fixed order),
+    // then the 4 waves through LDS.
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            float v = acc[j][c];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[j][c] = v;
+        }
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) < kRow) {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) wred[wid][j][lane * CH + c] = acc[j][c];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < R * D; o += 256) {
+        const int j = o / D, c = o - j * D;
+        const float v = ((wred[0][j][c] + wred[1][j][c]) + wred[2][j][c]) + wred[3][j][c];
+        part3[(((size_t)b * HQ + g * R + j) * nchunk3 + blockIdx.x) * D + c] = v;
+    }
+}
+
+__global__ void reduce_kernel(const float* __restrict__ part3, int HQ, int D, int nchunk3,
+                              float* __restrict__ out) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const size_t oh = (size_t)b * HQ + h;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        float s = 0.0f;
+        for (int k = 0; k < nchunk3; ++k) s += part3[(oh * nchunk3 + k) * D + c];
+        out[oh * D + c] = s;
+    }
+}
+
+// ---------------------------------------------------------------- host ----
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride) {
+    DecodePlan pl;
+    pl.sparse = sparse;
+    const int maxp = sparse ? sel_stride : d.MP;
+    pl.nslot = maxp * kPage;
+    pl.ppb = sparse ? 8 : 32;
+    pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
+    if (pl.nchunk1 < 1) pl.nchunk1 = 1;
+    pl.spb = sparse ? 256 : 4096;
+    pl.nchunk3 = (pl.nslot + pl.spb - 1) / pl.spb;
+    if (pl.nchunk3 < 1) pl.nchunk3 = 1;
+    const size_t bh = (size_t)d.B * d.HQ;
+    pl.off_logits = 0;
+    pl.off_part1 = align256(bh * pl.nslot * sizeof(float));
+    pl.off_part3 = pl.off_part1 + align256(bh * pl.nchunk1 * 3 * sizeof(float));
+    pl.bytes = pl.off_part3 + align256(bh * pl.nchunk3 * d.D * sizeof(float));
+    return pl;
+}
+
+template <typename T, int D, int R>
+static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* pt, const int32_t* sl,
+                             const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
+                             float alpha, int mode, float beta, const float* tau_ref, float* out,
+                             float* tau, int32_t* support, float* delta, char* ws, hipStream_t s) {
+    float* logits = (float*)(ws + pl.off_logits);
+    float* part1 = (float*)(ws + pl.off_part1);
+    float* part3 = (float*)(ws + pl.off_part3);
+    const int units = d.B * d.G;
+    logits_kernel<T, D, R><<<dim3(pl.nchunk1, units), dim3(256), 0, s>>>(
+        (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
+        pl.ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
+                                                     d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
+                                                     tau_ref, tau, support, delta);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(
+        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, tau, d.G, d.MP, d.NP,
+        pl.nslot, pl.spb, pl.nchunk3, mode, alpha, beta, part3);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    reduce_kernel<<<dim3(d.HQ, d.B), dim3(D), 0, s>>>(part3, d.HQ, D, pl.nchunk3, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
+                         float alpha, const float* tau_ref, float* out, float* tau,
+                         int32_t* support, float* delta, char* ws, hipStream_t s) {
+    int mode;
+    float beta = 0.0f;
+    if (alpha == 1.0f) {
+        mode = kModeSoftmax;
+    } else {
+        beta = 1.0f / (alpha - 1.0f);
+        mode = (beta == 1.0f) ? kModeBeta1 : (beta == 2.0f ? kModeBeta2 : kModeGeneral);
+    }
+#define EKV_DEC(RR, T, DD)                                                                       \
+    return run_decode<T, DD, RR>(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages,    \
+                                 sel_count, sel_stride, alpha, mode, beta, tau_ref, out, tau,     \
+                                 support, delta, ws, s)
+#define EKV_RSW(T, DD)                          \
+    switch (d.R) {                              \
+        case 1: EKV_DEC(1, T, DD);              \
+        case 2: EKV_DEC(2, T, DD);              \
+        case 4: EKV_DEC(4, T, DD);              \
+        case 8: EKV_DEC(8, T, DD);              \
+        default: return hipErrorInvalidValue;   \
+    }
+    if (d.kv_bf16) {
+        if (d.D == 128) { EKV_RSW(bf16_t, 128) } else { EKV_RSW(bf16_t, 64) }
+    } else {
+        if (d.D == 128) { EKV_RSW(float, 128) } else { EKV_RSW(float, 64) }
+    }
+#undef EKV_RSW
+#undef EKV_DEC
+}
+
+}  // namespace ekv

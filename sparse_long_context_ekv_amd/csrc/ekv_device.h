@@ -1,0 +1,176 @@
+// Device-side helpers for the libekv kernels (gfx950, wave64).
+//
+// Conventions used by every kernel:
+//  * a "row" is 16 consecutive lanes of a wavefront (one DPP row); a row
+//    covers one D-wide vector (a key, a value or a statistic) with each lane
+//    owning CH = D/16 consecutive channels, so a row reads D*sizeof(T)
+//    contiguous bytes;
+//  * reductions use fixed-order DPP rotations within a row and readlane /
+//    LDS across rows, never atomics, so every result is reproducible run to
+//    run;
+//  * bf16 values are carried as their 16-bit patterns (the upper half of an
+//    fp32), widened exactly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace ekv {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+constexpr int kPage = 16;     // tokens per page (the only page size built)
+constexpr int kRow = 16;      // lanes per DPP row
+
+// ---------------------------------------------------------------- loads ----
+// CH channels of element type T as 32-bit words.
+template <typename T, int CH>
+struct Vec {
+    static constexpr int NW = CH * (int)sizeof(T) / 4;
+    static_assert(NW == 2 || NW == 4 || NW == 8, "row slice must be 8, 16 or 32 bytes");
+    uint32_t w[NW];
+
+    __device__ __forceinline__ void load(const T* p) {
+        if constexpr (NW == 2) {
+            uint2 a = *reinterpret_cast<const uint2*>(p);
+            w[0] = a.x; w[1] = a.y;
+        } else if constexpr (NW == 4) {
+            uint4 a = *reinterpret_cast<const uint4*>(p);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        } else {
+            const uint4* p4 = reinterpret_cast<const uint4*>(p);
+            uint4 a = p4[0], b = p4[1];
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        }
+    }
+    __device__ __forceinline__ void store(T* p) const {
+        if constexpr (NW == 2) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+        } else if constexpr (NW == 4) {
+            *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            uint4* p4 = reinterpret_cast<uint4*>(p);
+            p4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            p4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
+    // Channel i widened to fp32 (exact).
+    __device__ __forceinline__ float get(int i) const {
+        if constexpr (std::is_same<T, float>::value) {
+            return __uint_as_float(w[i]);
+        } else {
+            return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u)
+                           : __uint_as_float(w[i >> 1] << 16);
+        }
+    }
+    // Set channel i from an fp32 value that is exactly representable in T.
+    __device__ __forceinline__ void set_exact(int i, float v) {
+        if constexpr (std::is_same<T, float>::value) {
+            w[i] = __float_as_uint(v);
+        } else {
+            uint32_t h = __float_as_uint(v) >> 16;
+            if (i & 1) w[i >> 1] = (w[i >> 1] & 0x0000ffffu) | (h << 16);
+            else       w[i >> 1] = (w[i >> 1] & 0xffff0000u) | h;
+        }
+    }
+};
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------- cross-lane ops ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls: row_ror:k = 0x120 + k.
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0x128>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x122>(v);
+    v += dpp<0x121>(v);
+    return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<0x128>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    v = fmaxf(v, dpp<0x122>(v));
+    v = fmaxf(v, dpp<0x121>(v));
+    return v;
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Wave-uniform sum / max over 64 lanes (fixed order: rows 0,1,2,3).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_sum16(v);
+    return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = row_max16(v);
+    return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+
+// Number of set bits of a 64-bit lane mask below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Block-uniform reductions for blocks of NW waves.  `red` is an LDS array
+// of at least 2*NW floats; `phase` alternates so that back-to-back calls need
+// one barrier each.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red, int& phase) {
+    float w = wave_sum(v);
+    const int wid = threadIdx.x >> 6;
+    float* r = red + phase * NW;
+    if ((threadIdx.x & 63) == 0) r[wid] = w;
+    __syncthreads();
+    float s = r[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) s += r[i];
+    phase ^= 1;
+    return s;
+}
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* red, int& phase) {
+    float w = wave_max(v);
+    const int wid = threadIdx.x >> 6;
+    float* r = red + phase * NW;
+    if ((threadIdx.x & 63) == 0) r[wid] = w;
+    __syncthreads();
+    float s = r[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) s = fmaxf(s, r[i]);
+    phase ^= 1;
+    return s;
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 == +0.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    if (f == 0.0f) f = 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int num_pages(int n) { return (n + kPage - 1) / kPage; }
+
+// Sequence length clamped to what its page-table row can address, so that a
+// bad length never sends a kernel outside the table, the cache or an output row.
+__device__ __forceinline__ int seq_len_at(const int32_t* seq_lens, int b, int MP) {
+    const int n = seq_lens[b];
+    const int cap = MP * kPage;
+    return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
+}  // namespace ekv

@@ -1,0 +1,56 @@
+// Host-side interface between the C ABI layer (api.hip) and the kernel
+// launchers (stats.hip, score.hip, select.hip, decode.hip).  Each launcher
+// enqueues its kernels on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ekv {
+
+struct Dims {
+    int B, HQ, G, R, D, MP, NP;
+    int kv_bf16;     // 1 = bf16 KV, 0 = fp32
+    int stat_bf16;   // 1 = bf16 mean/var, 0 = fp32
+};
+
+// Page statistics.
+hipError_t launch_page_stats(const Dims& d, const void* k_cache, const int32_t* page_table,
+                             const int32_t* seq_lens, const int32_t* page_list, int n_list,
+                             void* kmin, void* kmax, void* kmean, void* kvar, hipStream_t s);
+
+// Page scores.
+hipError_t launch_box_score(const Dims& d, const void* q, const int32_t* page_table,
+                            const int32_t* seq_lens, const void* kmin, const void* kmax,
+                            float* score, hipStream_t s);
+hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_table,
+                              const int32_t* seq_lens, const void* kmean, const void* kvar,
+                              float* mu, float* sigma, hipStream_t s);
+
+// Selection.  `keys` is workspace [B][G][MP] uint32.
+hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
+                            const int32_t* seq_lens, float alpha, float* tau_hat, hipStream_t s);
+hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, float alpha,
+                         int budget, float z, const float* score, const float* mu,
+                         const float* sigma, const float* tau_hat, uint32_t* keys,
+                         int32_t* sel_pages, int32_t* sel_count, hipStream_t s);
+
+// Decode.
+struct DecodePlan {
+    int sparse;      // selection given
+    int nslot;       // logits slots per (b, h)
+    int ppb;         // pages per logits block
+    int nchunk1;     // logits blocks per (b, g)
+    int spb;         // slots per PV block (multiple of 256)
+    int nchunk3;     // PV blocks per (b, g)
+    size_t off_logits, off_part1, off_part3, bytes;
+};
+DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride);
+hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
+                         float alpha, const float* tau_ref, float* out, float* tau,
+                         int32_t* support, float* delta, char* ws, hipStream_t s);
+
+}  // namespace ekv

@@ -1,0 +1,252 @@
+// Query-aware page scores.
+//
+// Box score ("EntmaxKV: Support-Aware Decoding for Entmax Attention",
+// section 4.2 and Appendix B.1): the largest q.k/sqrt(D) over the
+// axis-aligned box spanned by the page's keys,
+//     u_{h,p} = (1/sqrt(D)) sum_i max(q_i kmax_i, q_i kmin_i),
+// pooled per KV group by the maximum over the group's r query heads, so one
+// page set serves every head of the group.
+//
+// Gaussian moments (section 4.3, "score moments per head and batch element"
+// of section 4.4), channels treated as independent:
+//     mu_{h,p} = (1/sqrt(D)) sum_i q_i mean_i,  sigma_{h,p}^2 = (1/D) sum_i q_i^2 var_i.
+//
+// Both kernels are pure streams over the page statistics: one 16-lane row
+// per (page, group), lane l owning channels [l*CH, (l+1)*CH), the r query
+// slices of the group in registers, one fixed-order DPP row sum per head.
+// A block covers `ppb` consecutive logical pages of one sequence; each row
+// issues the loads of UNROLL pages before using any of them.
+#include "ekv_device.h"
+#include "ekv_internal.h"
+
+namespace ekv {
+
+constexpr int kUnroll = 4;
+
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void box_score_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const T* __restrict__ kmin, const T* __restrict__ kmax,
+    float* __restrict__ score, int G, int MP, int NP, int ppb, float inv_sqrt_d) {
+    constexpr int CH = D / kRow;
+    const int b = blockIdx.y;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const int p_begin = blockIdx.x * ppb;
+    if (p_begin >= M) return;
+    const int p_end = min(M, p_begin + ppb);
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    const int per_iter = kRow / G;
+    if (row >= per_iter * G) return;
+    const int slot = row / G, g = row % G;
+    const int HQ = G * R;
+
+    Vec<T, CH> qv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
+
+    // For bf16: per head and 32-bit word, a mask picking kmax where q >= 0
+    // and kmin where q < 0 (bitwise select), so max(q*kmax, q*kmin) is one
+    // select and one packed dot product per channel pair.
+    constexpr int NW = Vec<T, CH>::NW;
+    uint32_t pick_max[std::is_same<T, float>::value ? 1 : R][NW];
+    if constexpr (!std::is_same<T, float>::value) {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                uint32_t x = qv[j].w[w];
+                pick_max[j][w] = ((x & 0x8000u) ? 0u : 0x0000ffffu) | ((x & 0x80000000u) ? 0u : 0xffff0000u);
+            }
+    }
+    (void)pick_max;
+
+    const int32_t* pt = page_table + (size_t)b * MP;
+    float* out = score + ((size_t)b * G + g) * MP;
+    for (int p0 = p_begin + slot; p0 < p_end; p0 += kUnroll * per_iter) {
+        Vec<T, CH> lo[kUnroll], hi[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int p = p0 + u * per_iter;
+            int phys = p < p_end ? pt[p] : -1;
+            ok[u] = phys >= 0 && phys < NP;
+            if (ok[u]) {
+                const size_t off = ((size_t)phys * G + g) * D + lane * CH;
+                lo[u].load(kmin + off);
+                hi[u].load(kmax + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (!ok[u]) continue;
+            float best = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float acc = 0.0f;
+                if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        float qc = qv[j].get(c);
+                        acc = fmaf(qc, qc >= 0.0f ? hi[u].get(c) : lo[u].get(c), acc);
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        uint32_t m = pick_max[j][w];
+                        uint32_t sel = (m & hi[u].w[w]) | (~m & lo[u].w[w]);
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, sel),
+                                                              __builtin_bit_cast(bf16x2_t, qv[j].w[w]),
+                                                              acc, false);
+                    }
+                }
+                best = fmaxf(best, row_sum16(acc));
+            }
+            if (lane == 0) out[p0 + u * per_iter] = best * inv_sqrt_d;
+        }
+    }
+}
+
+template <typename T, typename S, int D, int R>
+__global__ __launch_bounds__(256) void gauss_score_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const S* __restrict__ kmean, const S* __restrict__ kvar,
+    float* __restrict__ mu, float* __restrict__ sigma, int G, int MP, int NP, int ppb,
+    float inv_sqrt_d, float inv_d) {
+    constexpr int CH = D / kRow;
+    const int b = blockIdx.y;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const int p_begin = blockIdx.x * ppb;
+    if (p_begin >= M) return;
+    const int p_end = min(M, p_begin + ppb);
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    const int per_iter = kRow / G;
+    if (row >= per_iter * G) return;
+    const int slot = row / G, g = row % G;
+    const int HQ = G * R;
+
+    float qf[R][CH], q2[R][CH];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        Vec<T, CH> v;
+        v.load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            qf[j][c] = v.get(c);
+            q2[j][c] = qf[j][c] * qf[j][c];
+        }
+    }
+
+    const int32_t* pt = page_table + (size_t)b * MP;
+    // lane j < R writes mu of head g*R+j, lane R+j writes its sigma
+    const int jh = lane < R ? lane : lane - R;
+    float* dst = (lane < R ? mu : sigma) + ((size_t)b * HQ + g * R + jh) * MP;
+    const bool writer = lane < 2 * R;
+    for (int p0 = p_begin + slot; p0 < p_end; p0 += kUnroll * per_iter) {
+        Vec<S, CH> mv[kUnroll], vv[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int p = p0 + u * per_iter;
+            int phys = p < p_end ? pt[p] : -1;
+            ok[u] = phys >= 0 && phys < NP;
+            if (ok[u]) {
+                const size_t off = ((size_t)phys * G + g) * D + lane * CH;
+                mv[u].load(kmean + off);
+                vv[u].load(kvar + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (!ok[u]) continue;
+            float mine = 0.0f;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float am = 0.0f, av = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    am = fmaf(qf[j][c], mv[u].get(c), am);
+                    av = fmaf(q2[j][c], vv[u].get(c), av);
+                }
+                am = row_sum16(am);
+                av = row_sum16(av);
+                mine = (lane == j) ? am * inv_sqrt_d : mine;
+                mine = (lane == R + j) ? sqrtf(fmaxf(av, 0.0f) * inv_d) : mine;
+            }
+            if (writer) dst[p0 + u * per_iter] = mine;
+        }
+    }
+}
+
+static int score_ppb(const Dims& d) {
+    // Enough blocks to fill 256 CUs several times over, at most 256 pages each.
+    long units = (long)d.B * d.MP;
+    int ppb = 64;
+    while (ppb > 8 && units / ppb < 4096) ppb >>= 1;
+    return ppb;
+}
+
+template <typename T, int D, int R>
+static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
+                          const void* kmin, const void* kmax, float* score, hipStream_t s) {
+    const int ppb = score_ppb(d);
+    dim3 grid((d.MP + ppb - 1) / ppb, d.B);
+    box_score_kernel<T, D, R><<<grid, dim3(256), 0, s>>>((const T*)q, pt, sl, (const T*)kmin, (const T*)kmax,
+                                                         score, d.G, d.MP, d.NP, ppb, 1.0f / sqrtf((float)D));
+    return hipGetLastError();
+}
+
+template <typename T, typename S, int D, int R>
+static hipError_t run_gauss(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
+                            const void* kmean, const void* kvar, float* mu, float* sigma, hipStream_t s) {
+    const int ppb = score_ppb(d);
+    dim3 grid((d.MP + ppb - 1) / ppb, d.B);
+    gauss_score_kernel<T, S, D, R><<<grid, dim3(256), 0, s>>>((const T*)q, pt, sl, (const S*)kmean, (const S*)kvar,
+                                                              mu, sigma, d.G, d.MP, d.NP, ppb,
+                                                              1.0f / sqrtf((float)D), 1.0f / (float)D);
+    return hipGetLastError();
+}
+
+#define EKV_R_SWITCH(MACRO, ...)                          \
+    switch (d.R) {                                        \
+        case 1: MACRO(1, __VA_ARGS__);                    \
+        case 2: MACRO(2, __VA_ARGS__);                    \
+        case 4: MACRO(4, __VA_ARGS__);                    \
+        case 8: MACRO(8, __VA_ARGS__);                    \
+        default: return hipErrorInvalidValue;             \
+    }
+
+hipError_t launch_box_score(const Dims& d, const void* q, const int32_t* page_table,
+                            const int32_t* seq_lens, const void* kmin, const void* kmax,
+                            float* score, hipStream_t s) {
+#define EKV_BOX(RR, T, DD) return run_box<T, DD, RR>(d, q, page_table, seq_lens, kmin, kmax, score, s)
+    if (d.kv_bf16) {
+        if (d.D == 128) { EKV_R_SWITCH(EKV_BOX, bf16_t, 128) } else { EKV_R_SWITCH(EKV_BOX, bf16_t, 64) }
+    } else {
+        if (d.D == 128) { EKV_R_SWITCH(EKV_BOX, float, 128) } else { EKV_R_SWITCH(EKV_BOX, float, 64) }
+    }
+#undef EKV_BOX
+}
+
+hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_table,
+                              const int32_t* seq_lens, const void* kmean, const void* kvar,
+                              float* mu, float* sigma, hipStream_t s) {
+#define EKV_GS(RR, T, S, DD) return run_gauss<T, S, DD, RR>(d, q, page_table, seq_lens, kmean, kvar, mu, sigma, s)
+    if (d.kv_bf16) {
+        if (d.stat_bf16) {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 64) }
+        } else {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, float, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, float, 64) }
+        }
+    } else {
+        if (d.stat_bf16) {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, float, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GS, float, bf16_t, 64) }
+        } else {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, float, float, 128) } else { EKV_R_SWITCH(EKV_GS, float, float, 64) }
+        }
+    }
+#undef EKV_GS
+}
+
+}  // namespace ekv

@@ -1,0 +1,144 @@
+// Page key statistics: per (physical page, group, channel) min / max / mean /
+// population variance over the page's valid tokens.
+//
+// Follows "EntmaxKV: Support-Aware Decoding for Entmax Attention" section 4.2
+// and Appendix B.1 (per-channel page min/max of the keys) and section 4.3
+// (per-page mean/variance read by the Gaussian selector).
+//
+// Mapping: one 16-lane row per (page, group) tile; lane l owns channels
+// [l*CH, (l+1)*CH) and walks the page's 16 token rows, so each token row is
+// one contiguous D*sizeof(T)-byte read by the 16 lanes.  The whole tile stays
+// in registers: min/max are exact selections of stored values, the mean is an
+// fp32 sum in token order divided by n_p, the variance a second pass over the
+// registers (sum of squared deviations / n_p).
+#include "ekv_device.h"
+#include "ekv_internal.h"
+
+namespace ekv {
+
+template <typename T, int D, typename S>
+__global__ __launch_bounds__(256) void page_stats_kernel(
+    const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_list, int n_items,
+    int B, int G, int MP, int NP, T* __restrict__ kmin, T* __restrict__ kmax, S* __restrict__ kmean,
+    S* __restrict__ kvar) {
+    constexpr int CH = D / kRow;
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    const int per_iter = kRow / G;               // (page) items per block iteration
+    if (row >= per_iter * G) return;             // whole idle rows only
+    const int g = row % G;
+    for (int item = blockIdx.x * per_iter + row / G; item < n_items; item += gridDim.x * per_iter) {
+        int e = page_list ? page_list[item] : item;
+        int b = e / MP, p = e - b * MP;
+        if (b < 0 || b >= B) continue;
+        int n = seq_len_at(seq_lens, b, MP);
+        if (p >= num_pages(n)) continue;
+        int np = min(kPage, n - p * kPage);
+        int phys = page_table[(size_t)b * MP + p];
+        if (phys < 0 || phys >= NP) continue;     // corrupt table entry: never read outside the cache
+        const T* tile = k_cache + ((size_t)phys * G + g) * kPage * D + lane * CH;
+
+        Vec<T, CH> v[kPage];
+#pragma unroll
+        for (int t = 0; t < kPage; ++t)
+            if (t < np) v[t].load(tile + (size_t)t * D);
+
+        float mn[CH], mx[CH], sm[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            mn[c] = v[0].get(c);
+            mx[c] = mn[c];
+            sm[c] = mn[c];
+        }
+#pragma unroll
+        for (int t = 1; t < kPage; ++t) {
+            if (t < np) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    float x = v[t].get(c);
+                    mn[c] = fminf(mn[c], x);
+                    mx[c] = fmaxf(mx[c], x);
+                    sm[c] += x;
+                }
+            }
+        }
+        float mean[CH], var[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            mean[c] = sm[c] / (float)np;
+            var[c] = 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < kPage; ++t) {
+            if (t < np) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    float dlt = v[t].get(c) - mean[c];
+                    var[c] = fmaf(dlt, dlt, var[c]);
+                }
+            }
+        }
+        const size_t out = ((size_t)phys * G + g) * D + lane * CH;
+        if (kmin) {
+            Vec<T, CH> a, c2;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                a.set_exact(c, mn[c]);
+                c2.set_exact(c, mx[c]);
+            }
+            a.store(kmin + out);
+            c2.store(kmax + out);
+        }
+        if (kmean) {
+            if constexpr (std::is_same<S, float>::value) {
+#pragma unroll
+                for (int c = 0; c < CH; c += 4) {
+                    *reinterpret_cast<float4*>(kmean + out + c) = make_float4(mean[c], mean[c + 1], mean[c + 2], mean[c + 3]);
+                    *reinterpret_cast<float4*>(kvar + out + c) =
+                        make_float4(var[c] / (float)np, var[c + 1] / (float)np, var[c + 2] / (float)np, var[c + 3] / (float)np);
+                }
+            } else {
+                Vec<bf16_t, CH> a, c2;
+#pragma unroll
+                for (int c = 0; c < CH; c += 2) {
+                    a.w[c >> 1] = f32_to_bf16_rne(mean[c]) | (f32_to_bf16_rne(mean[c + 1]) << 16);
+                    c2.w[c >> 1] = f32_to_bf16_rne(var[c] / (float)np) | (f32_to_bf16_rne(var[c + 1] / (float)np) << 16);
+                }
+                a.store(reinterpret_cast<bf16_t*>(kmean) + out);
+                c2.store(reinterpret_cast<bf16_t*>(kvar) + out);
+            }
+        }
+    }
+}
+
+template <typename T, int D, typename S>
+static hipError_t run_stats(const Dims& d, const void* k, const int32_t* pt, const int32_t* sl,
+                            const int32_t* pl, int n_items, void* kmin, void* kmax, void* kmean,
+                            void* kvar, hipStream_t s) {
+    const int per_iter = kRow / d.G;
+    long blocks = ((long)n_items + per_iter - 1) / per_iter;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    page_stats_kernel<T, D, S><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        (const T*)k, pt, sl, pl, n_items, d.B, d.G, d.MP, d.NP, (T*)kmin, (T*)kmax, (S*)kmean, (S*)kvar);
+    return hipGetLastError();
+}
+
+hipError_t launch_page_stats(const Dims& d, const void* k_cache, const int32_t* page_table,
+                             const int32_t* seq_lens, const int32_t* page_list, int n_list,
+                             void* kmin, void* kmax, void* kmean, void* kvar, hipStream_t s) {
+    const int n_items = page_list ? n_list : d.B * d.MP;
+    if (n_items <= 0) return hipSuccess;
+#define EKV_STATS(T, DD, S) return run_stats<T, DD, S>(d, k_cache, page_table, seq_lens, page_list, n_items, kmin, kmax, kmean, kvar, s)
+    if (d.kv_bf16) {
+        if (d.D == 128) { if (d.stat_bf16) EKV_STATS(bf16_t, 128, bf16_t); else EKV_STATS(bf16_t, 128, float); }
+        else            { if (d.stat_bf16) EKV_STATS(bf16_t, 64, bf16_t);  else EKV_STATS(bf16_t, 64, float); }
+    } else {
+        if (d.D == 128) { if (d.stat_bf16) EKV_STATS(float, 128, bf16_t); else EKV_STATS(float, 128, float); }
+        else            { if (d.stat_bf16) EKV_STATS(float, 64, bf16_t);  else EKV_STATS(float, 64, float); }
+    }
+#undef EKV_STATS
+}
+
+}  // namespace ekv

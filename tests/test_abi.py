@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ekv.h declares, rejects bad arguments on the host before any HIP
+call, and answers workspace queries.  (Compute calls need a GPU and live in
+the gpu-marked tests.)"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_context_ekv_amd import ekv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ekv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ekv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ekv.LIB_PATH):
+        pytest.fail("libekv.so is not built (run python -m sparse_long_context_ekv_amd.build)")
+    return ekv.load()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.ekv_abi_version() == 1
+
+
+def _shape(**kw):
+    base = dict(batch=2, num_q_heads=32, num_kv_groups=8, head_dim=128, max_pages_per_seq=64,
+                num_phys_pages=128, kv_dtype="bf16", stat_dtype="f32")
+    base.update(kw)
+    return ekv.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), ekv.ERR_INVALID_ARG),          # not a multiple of G
+    (dict(num_q_heads=24), ekv.ERR_UNSUPPORTED),          # r = 3
+    (dict(head_dim=96), ekv.ERR_UNSUPPORTED),
+    (dict(page_size=8), ekv.ERR_UNSUPPORTED),
+    (dict(batch=0), ekv.ERR_INVALID_ARG),
+    (dict(num_kv_groups=32, num_q_heads=32), ekv.ERR_UNSUPPORTED),
+])
+def test_shape_validation(lib, kw, status):
+    page_size = kw.pop("page_size", 16)
+    sh = _shape(**kw)
+    sh.page_size = page_size
+    n = ctypes.c_size_t(0)
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), None, None, None, None, None, None, None, 0, 1.5, None,
+                               None, None, None, None, None, ctypes.byref(n), None)
+    assert st == status
+    assert lib.ekv_last_error().decode() != ""
+
+
+def test_bad_dtype_rejected(lib):
+    sh = _shape()
+    sh.kv_dtype = 7
+    with pytest.raises(ekv.EkvError) as e:
+        ekv.decode_workspace_bytes(sh, False, 0)
+    assert e.value.status == ekv.ERR_UNSUPPORTED
+
+
+def test_null_required_pointers_rejected_before_launch(lib):
+    sh = _shape()
+    st = lib.ekv_build_page_stats(ctypes.byref(sh), None, None, None, None, 0, None, None, None, None, None)
+    assert st == ekv.ERR_INVALID_ARG
+    st = lib.ekv_build_page_stats(ctypes.byref(sh), 8, 8, 8, None, 0, 8, None, None, None, None)
+    assert st == ekv.ERR_INVALID_ARG                       # kmin without kmax
+    st = lib.ekv_score_pages(ctypes.byref(sh), ekv.SEL_TOPK, 8, 8, 8, None, None, None, None, None, None, None, None)
+    assert st == ekv.ERR_INVALID_ARG
+    st = lib.ekv_score_pages(ctypes.byref(sh), 5, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None)
+    assert st == ekv.ERR_INVALID_ARG
+    assert lib.ekv_score_pages(None, 0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None) == ekv.ERR_INVALID_ARG
+
+
+def test_select_argument_checks(lib):
+    sh = _shape()
+    n = ctypes.c_size_t(0)
+    assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_TOPK, None, 1.5, 0, 3.0, None, None, None, None, None,
+                          None, None, ctypes.byref(n), None) == ekv.ERR_INVALID_ARG      # budget 0
+    assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_GAUSS, None, 1.7, 8, 3.0, None, None, None, None, None,
+                          None, None, ctypes.byref(n), None) == ekv.ERR_UNSUPPORTED      # alpha 1.7
+    assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_GAUSS, None, 1.0, 8, 3.0, None, None, None, None, None,
+                          None, None, ctypes.byref(n), None) == ekv.ERR_INVALID_ARG      # softmax + Gaussian
+    assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_TOPK, None, 1.5, 8, 3.0, None, None, None, None, None,
+                          None, None, None, None) == ekv.ERR_INVALID_ARG                 # no size pointer
+
+
+def test_select_workspace_query(lib):
+    sh = _shape()
+    need_topk = ekv.select_workspace_bytes(sh, ekv.SEL_TOPK, 1.5, 8)
+    need_gauss = ekv.select_workspace_bytes(sh, ekv.SEL_GAUSS, 1.5, 8)
+    assert need_topk >= 2 * 8 * 64 * 4 and need_topk % 256 == 0
+    assert need_gauss > need_topk
+    assert ekv.select_workspace_bytes(sh, ekv.SEL_TOPK, 1.5, 8) == need_topk     # idempotent
+    n = ctypes.c_size_t(need_topk - 1)
+    st = lib.ekv_select(ctypes.byref(sh), ekv.SEL_TOPK, 8, 1.5, 8, 3.0, 8, None, None, 8, 8, None, 256,
+                        ctypes.byref(n), None)
+    assert st == ekv.ERR_WORKSPACE
+
+
+def test_decode_workspace_query_and_checks(lib):
+    sh = _shape()
+    sparse = ekv.decode_workspace_bytes(sh, True, 16)
+    full = ekv.decode_workspace_bytes(sh, False, 0)
+    assert 0 < sparse < full
+    assert ekv.decode_workspace_bytes(sh, True, 16) == sparse
+    n = ctypes.c_size_t(sparse - 1)
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, None, 256,
+                               ctypes.byref(n), None)
+    assert st == ekv.ERR_WORKSPACE
+    n = ctypes.c_size_t(sparse)
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, 8, 256,
+                               ctypes.byref(n), None)
+    assert st == ekv.ERR_INVALID_ARG                       # delta without tau_ref
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, 8, 8, None, None, 256,
+                               ctypes.byref(n), None)
+    assert st == ekv.ERR_INVALID_ARG                       # alpha < 1
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, None, 300,
+                               ctypes.byref(n), None)
+    assert st == ekv.ERR_INVALID_ARG                       # misaligned workspace
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, 8, 8, None, None, 256,
+                               ctypes.byref(n), None)
+    assert st == ekv.ERR_INVALID_ARG                       # sel_pages without sel_count
