@@ -325,8 +325,13 @@ def test_bitwise_reproducible():
     dec.step()
     H.sync()
     b = (dec.buf.out, dec.buf.tau, dec.buf.sel_pages, dec.buf.score)
-    for x, y in zip(a, b):
+    for x, y in zip(a[:3], b[:3]):
         assert torch.equal(x, y)
+    # score entries past a sequence's last page are never written: compare
+    # only the written ones (the rest hold whatever the buffer held).
+    for bb, n in enumerate(wl.seq_lens_host):
+        M = (n + P - 1) // P
+        assert torch.equal(a[3][bb, :, :M], b[3][bb, :, :M])
 
 
 def test_physical_placement_invariance():
