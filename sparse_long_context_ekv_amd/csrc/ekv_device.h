@@ -156,6 +156,101 @@ __device__ __forceinline__ float block_max(float v, float* red, int& phase) {
     return s;
 }
 
+// Two block-uniform sums with one barrier.  `red` holds at least 4*NW floats.
+template <int NW>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red, int& phase) {
+    const float wa = wave_sum(a), wb = wave_sum(b);
+    const int wid = threadIdx.x >> 6;
+    float* r = red + phase * 2 * NW;
+    if ((threadIdx.x & 63) == 0) {
+        r[wid] = wa;
+        r[NW + wid] = wb;
+    }
+    __syncthreads();
+    float sa = r[0], sb = r[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        sa += r[i];
+        sb += r[NW + i];
+    }
+    phase ^= 1;
+    a = sa;
+    b = sb;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele on
+// shuffles; integer, so the order does not matter).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Block-wide exclusive prefix sums of two per-thread counts, in thread
+// order, for blocks of NW waves; totals are returned in *ta, *tb.  `wsum`
+// is LDS of at least 2*NW ints.  Ends with a barrier, so `wsum` may be
+// reused right after.
+template <int NW>
+__device__ __forceinline__ void block_excl_scan2(int a, int b, int& ea, int& eb, int* ta, int* tb, int* wsum) {
+    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 63) {
+        wsum[wid] = ia;
+        wsum[NW + wid] = ib;
+    }
+    __syncthreads();
+    int oa = 0, ob = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int ca = wsum[i], cb = wsum[NW + i];
+        oa += i < wid ? ca : 0;
+        ob += i < wid ? cb : 0;
+        sa += ca;
+        sb += cb;
+    }
+    __syncthreads();
+    ea = oa + ia - a;
+    eb = ob + ib - b;
+    *ta = sa;
+    *tb = sb;
+}
+
+// Block-wide total of a per-thread count and min / max of per-thread uint32
+// values, for blocks of NW waves; every thread gets the results.  `wsum` is
+// LDS of at least 3*NW ints.  Ends with a barrier.
+template <int NW>
+__device__ __forceinline__ void block_count_range(int c, uint32_t& mn, uint32_t& mx, int* total, int* wsum) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        c += __shfl_xor(c, off, 64);
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    }
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        wsum[wid] = c;
+        wsum[NW + wid] = (int)mn;
+        wsum[2 * NW + wid] = (int)mx;
+    }
+    __syncthreads();
+    int t = 0;
+    uint32_t a = 0xffffffffu, b = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        t += wsum[i];
+        a = min(a, (uint32_t)wsum[NW + i]);
+        b = max(b, (uint32_t)wsum[2 * NW + i]);
+    }
+    __syncthreads();
+    *total = t;
+    mn = a;
+    mx = b;
+}
+
 // Order-preserving map float -> uint32 (larger float, larger key); -0 == +0.
 __device__ __forceinline__ uint32_t ord_key(float f) {
     if (f == 0.0f) f = 0.0f;

@@ -9,12 +9,13 @@
 // m = (alpha-1) mu - tau, v = (alpha-1) sigma, z = m/v):
 //     E1 = m Phi + v phi,  E2 = (m^2 + v^2) Phi + m v phi,
 //     E3 = (m^3 + 3 m v^2) Phi + v (m^2 + 2 v^2) phi,   v = 0: [m]_+^beta.
-// F is convex and decreasing in tau and F(max_p (alpha-1) mu_p - 1) >= 0
-// (Jensen on the page with the largest mean), so Newton steps taken from that
-// point increase monotonically to the root; dF/dtau = -beta sum n_p E_{beta-1}.
+// F is decreasing in tau, dF/dtau = -beta sum n_p E_{beta-1}, and
+// F(max_p (alpha-1) mu_p - 1) >= 1 (Jensen on the page with the largest mean),
+// which starts a bracketed Newton iteration on log F (see gauss_tau_kernel).
 // The page moments are staged in LDS when they fit.
 //
-// select_kernel: one block per (sequence, KV group).  Keys are the pooled box
+// select_reg_kernel / select_kernel: one block per (sequence, KV group).
+// Keys are the pooled box
 // score (top-k) or the pooled Gaussian margin
 //     t_p = max_h (mu_{h,p} - tau_hat_h/(alpha-1)) / sigma_{h,p}
 // (Gaussian; sigma = 0 gives +inf when mu > theta, else -inf).  Pages with a
@@ -28,40 +29,87 @@
 
 namespace ekv {
 
-constexpr int kTauThreads = 256;
-constexpr int kTauLdsPages = 8192;     // 64 KiB of LDS for (a*mu, a*sigma)
+constexpr int kTauThreads = 512;
+constexpr int kTauWaves = kTauThreads / 64;
+constexpr int kTauLdsPages = 8192;     // 64 KiB of LDS for the (a*mu, a*sigma) pairs
+constexpr int kTauMaxIter = 40;
+constexpr float kTauTol = 1e-5f;       // stop once a step is below this (relative)
 
-__device__ __forceinline__ void gauss_terms(int beta, float m, float v, float& e_b, float& e_bm1) {
-    if (v > 0.0f) {
-        const float z = m / v;
-        const float Phi = 0.5f * erfcf(-z * 0.70710678118654752f);
-        const float phi = 0.39894228040143268f * expf(-0.5f * z * z);
-        const float e1 = fmaf(m, Phi, v * phi);
-        if (beta == 1) {
-            e_b = e1;
-            e_bm1 = Phi;
-        } else {
-            const float e2 = fmaf(fmaf(m, m, v * v), Phi, m * v * phi);
-            if (beta == 2) {
-                e_b = e2;
-                e_bm1 = e1;
-            } else {
-                e_b = fmaf(m * fmaf(m, m, 3.0f * v * v), Phi, v * fmaf(m, m, 2.0f * v * v) * phi);
-                e_bm1 = e2;
-            }
-        }
+// Standard normal upper tail Q(x) = 1 - Phi(x), x >= 0, as phi(x) R(x) with
+// the Mills ratio R(x) ~ t h(t), t = 1/(1 + kMillsK x), h the polynomial
+// below (fitted by fit_mills_ratio.py beside this file; relative error of R
+// about 3e-7 in fp32 over all x >= 0).
+constexpr float kMillsK = 0.4f;
+constexpr float kMillsC[12] = {
+    4.000000060e-01f, 3.999997675e-01f, 3.360165060e-01f, 2.075455040e-01f,
+    5.289435759e-02f, -1.341597885e-01f, 1.025012210e-01f, -7.160952091e-01f,
+    1.344201684e+00f, -1.132010460e+00f, 4.732496738e-01f, -8.082909137e-02f};
+constexpr float kTinyV = 1e-30f;       // v at or below this: the page is a point mass
+
+// n_p-free terms of page p at threshold tau, with m = (alpha-1) mu_p - tau,
+// v = (alpha-1) sigma_p, z = m/v: e_b = E[Y_+^beta], e_bm1 = E[Y_+^(beta-1)]
+// for Y ~ N(m, v^2) (E[Y_+^0] = P(Y > 0) = Phi(z)).  A page with v <= kTinyV
+// is a point mass at m: E[Y_+^k] = [m]_+^k.  Branch-free: both forms are
+// computed and one is selected.
+template <int BETA>
+__device__ __forceinline__ void gauss_terms(float m, float v, float& e_b, float& e_bm1) {
+    const bool point = !(v > kTinyV);
+    const float vs = point ? 1.0f : v;
+    const float z = m * __builtin_amdgcn_rcpf(vs);
+    const float t = __builtin_amdgcn_rcpf(fmaf(kMillsK, fabsf(z), 1.0f));
+    float h = kMillsC[11];
+#pragma unroll
+    for (int i = 10; i >= 0; --i) h = fmaf(h, t, kMillsC[i]);
+    // phi(z) = exp(-z^2/2) / sqrt(2 pi), through 2^x
+    const float phi = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z);
+    const float q = phi * t * h;
+    const float Phi = z < 0.0f ? q : 1.0f - q;
+    const float mp = fmaxf(m, 0.0f);
+    const float e1 = fmaf(m, Phi, vs * phi);
+    if constexpr (BETA == 1) {
+        e_b = point ? mp : e1;
+        e_bm1 = point ? (m > 0.0f ? 1.0f : 0.0f) : Phi;
     } else {
-        const float mp = fmaxf(m, 0.0f);
-        e_bm1 = beta == 1 ? (m > 0.0f ? 1.0f : 0.0f) : (beta == 2 ? mp : mp * mp);
-        e_b = e_bm1 * mp;
+        const float e2 = fmaf(fmaf(m, m, vs * vs), Phi, m * vs * phi);
+        if constexpr (BETA == 2) {
+            e_b = point ? mp * mp : e2;
+            e_bm1 = point ? mp : e1;
+        } else {
+            const float e3 = fmaf(m * fmaf(m, m, 3.0f * vs * vs), Phi, vs * fmaf(m, m, 2.0f * vs * vs) * phi);
+            e_b = point ? mp * mp * mp : e3;
+            e_bm1 = point ? mp * mp : e2;
+        }
     }
 }
 
+// Sums over the pages of this thread: F += n_p e_beta, D += n_p e_(beta-1).
+// Two pages per trip; only the sequence's last page can be partial.
+template <int BETA, bool STAGED>
+__device__ __forceinline__ void gauss_sums(const float2* __restrict__ lds2, const float* __restrict__ mrow,
+                                           const float* __restrict__ srow, int M, float a, float last_np,
+                                           float t, float& f, float& dsum) {
+    auto page = [&](int p) {
+        const float2 e = STAGED ? lds2[p] : make_float2(a * mrow[p], a * srow[p]);
+        const float np = (p == M - 1) ? last_np : (float)kPage;
+        float eb, ebm1;
+        gauss_terms<BETA>(e.x - t, e.y, eb, ebm1);
+        f = fmaf(np, eb, f);
+        dsum = fmaf(np, ebm1, dsum);
+    };
+    int p = threadIdx.x;
+    for (; p + kTauThreads < M; p += 2 * kTauThreads) {
+        page(p);
+        page(p + kTauThreads);
+    }
+    if (p < M) page(p);
+}
+
+template <int BETA>
 __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
     const float* __restrict__ mu, const float* __restrict__ sigma, const int32_t* __restrict__ seq_lens,
-    int HQ, int MP, float a, int beta, int lds_pages, float* __restrict__ tau_hat) {
-    extern __shared__ float lds[];                 // [2][kTauLdsPages] when staged
-    __shared__ float red[16];
+    int HQ, int MP, float a, int lds_pages, float* __restrict__ tau_hat) {
+    extern __shared__ float2 lds2[];               // [lds_pages] (a*mu, a*sigma) when staged
+    __shared__ float red[4 * kTauWaves];
     int phase = 0;
     const int h = blockIdx.x, b = blockIdx.y;
     const int n = seq_len_at(seq_lens, b, MP);
@@ -71,45 +119,47 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
         if (threadIdx.x == 0) *out = -INFINITY;
         return;
     }
-    const int last_np = n - (M - 1) * kPage;
+    const float last_np = (float)(n - (M - 1) * kPage);
     const float* mrow = mu + ((size_t)b * HQ + h) * MP;
     const float* srow = sigma + ((size_t)b * HQ + h) * MP;
     const bool staged = M <= lds_pages;
-    float* lm = lds;
-    float* ls = lds + lds_pages;
 
     float xmax = -INFINITY;
     for (int p = threadIdx.x; p < M; p += kTauThreads) {
-        float xm = a * mrow[p];
+        const float xm = a * mrow[p];
         xmax = fmaxf(xmax, xm);
-        if (staged) {
-            lm[p] = xm;
-            ls[p] = a * srow[p];
-        }
+        if (staged) lds2[p] = make_float2(xm, a * srow[p]);
     }
-    xmax = block_max<kTauThreads / 64>(xmax, red, phase);   // barrier also publishes LDS
-    float tau = xmax - 1.0f;
-    for (int it = 0; it < 64; ++it) {
-        float f = 0.0f, df = 0.0f;
-        for (int p = threadIdx.x; p < M; p += kTauThreads) {
-            const float xm = staged ? lm[p] : a * mrow[p];
-            const float v = staged ? ls[p] : a * srow[p];
-            const float np = (p == M - 1) ? (float)last_np : (float)kPage;
-            float eb, ebm1;
-            gauss_terms(beta, xm - tau, v, eb, ebm1);
-            f = fmaf(np, eb, f);
-            df = fmaf(np, ebm1, df);
+    xmax = block_max<kTauWaves>(xmax, red, phase);   // barrier also publishes LDS
+
+    constexpr float fb = (float)BETA;
+    float lo = xmax - 1.0f, hi = INFINITY, t = lo;   // F(lo) >= 1 (Jensen on the top page)
+    for (int it = 0; it < kTauMaxIter; ++it) {
+        float f = 0.0f, dsum = 0.0f;
+        if (staged) gauss_sums<BETA, true>(lds2, mrow, srow, M, a, last_np, t, f, dsum);
+        else        gauss_sums<BETA, false>(lds2, mrow, srow, M, a, last_np, t, f, dsum);
+        block_sum2<kTauWaves>(f, dsum, red, phase);   // block-uniform from here on
+        if (f >= 1.0f) lo = t; else hi = t;
+        if (f == 1.0f) break;
+        float step = NAN;
+        if (dsum > 0.0f && f > 0.0f) {
+            step = logf(f) * f / (fb * dsum);
+            if (f > 1.0f) {
+                const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
+                step = fminf(step, 4.0f * (1.0f - 1.0f / gr) * f / dsum);
+            }
         }
-        f = block_sum<kTauThreads / 64>(f, red, phase) - 1.0f;
-        df = block_sum<kTauThreads / 64>(df, red, phase) * (float)beta;
-        if (!(f > 0.0f) || !(df > 0.0f)) break;     // at the root (to rounding)
-        const float nt = tau + f / df;
-        if (!(nt > tau)) break;                       // no further fp32 progress
-        const bool done = (nt - tau) <= 1e-7f * fmaxf(1.0f, fabsf(nt));
-        tau = nt;
+        float nt = t + step;
+        if (!(nt >= lo && nt <= hi)) {
+            if (!(hi < INFINITY)) break;          // no usable step and no upper end yet
+            nt = 0.5f * (lo + hi);
+            step = nt - t;
+        }
+        const bool done = fabsf(step) <= kTauTol * fmaxf(1.0f, fabsf(t));
+        t = nt;
         if (done) break;
     }
-    if (threadIdx.x == 0) *out = tau;
+    if (threadIdx.x == 0) *out = t;
 }
 
 // --------------------------------------------------------------- select ----
@@ -263,30 +313,225 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (threadIdx.x == 0) sel_count[(size_t)b * G + g] = min(written, budget);
 }
 
+// KPT consecutive floats of `row` starting at p0 (entries at or past M read
+// as 0 and are never used); 16-byte loads when the whole span is valid and
+// aligned.
+template <int KPT>
+__device__ __forceinline__ void load_span(const float* __restrict__ row, int p0, int M, float (&v)[KPT]) {
+    if (p0 + KPT <= M && ((uintptr_t)(row + p0) & 15) == 0) {
+#pragma unroll
+        for (int j = 0; j < KPT; j += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(row + p0 + j);
+            v[j] = x.x;
+            v[j + 1] = x.y;
+            v[j + 2] = x.z;
+            v[j + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) v[j] = p0 + j < M ? row[p0 + j] : 0.0f;
+    }
+}
+
+// Same selection as select_kernel with the keys held in registers: thread t
+// owns the KPT consecutive pages [t*KPT, (t+1)*KPT), so one block-wide scan of
+// per-thread counts places every kept page in ascending order.  Needs
+// M <= KPT * kSelThreads.
+template <int GAUSS, int R, int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
+    const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
+    const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
+    float inv_a, float zcut, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
+    __shared__ int hist[256];
+    __shared__ int wsum[3 * kSelWaves];
+    __shared__ int sh_digit, sh_above;
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int HQ = G * R;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    int32_t* out = sel_pages + ((size_t)b * G + g) * budget;
+    const int p0 = threadIdx.x * KPT;
+
+    // Keys: pooled box score, or pooled Gaussian margin.
+    uint32_t key[KPT];
+    if constexpr (GAUSS) {
+        constexpr int C = KPT < 8 ? KPT : 8;      // pages per sub-chunk (bounds registers)
+#pragma unroll
+        for (int c0 = 0; c0 < KPT; c0 += C) {
+            float f[C];
+#pragma unroll
+            for (int i = 0; i < C; ++i) f[i] = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const size_t o = ((size_t)b * HQ + g * R + j) * MP;
+                const float theta = tau_hat[(size_t)b * HQ + g * R + j] * inv_a;
+                float m[C], sg[C];
+                load_span<C>(mu + o, p0 + c0, M, m);
+                load_span<C>(sigma + o, p0 + c0, M, sg);
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    const float dm = m[i] - theta;
+                    const float t = sg[i] > 0.0f ? dm / sg[i] : (dm > 0.0f ? INFINITY : -INFINITY);
+                    f[i] = fmaxf(f[i], t);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < C; ++i) key[c0 + i] = ord_key(f[i]);
+        }
+    } else {
+        float f[KPT];
+        load_span<KPT>(score + ((size_t)b * G + g) * MP, p0, M, f);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) key[i] = ord_key(f[i]);
+    }
+
+    // Candidates (key >= cut): their count and key range.
+    const uint32_t cut = GAUSS ? ord_key(-zcut) : 0u;
+    int cnt = 0;
+    uint32_t cmin = 0xffffffffu, cmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (p0 + i < M && key[i] >= cut) {
+            ++cnt;
+            cmin = min(cmin, key[i]);
+            cmax = max(cmax, key[i]);
+        }
+    }
+    int ncand;
+    block_count_range<kSelWaves>(cnt, cmin, cmax, &ncand, wsum);
+    const int keep = M == 0 ? 0 : max(1, min(budget, ncand));
+
+    uint32_t T;
+    int need_eq;
+    if (ncand >= 1 && ncand <= budget) {
+        T = cut;              // every candidate, nothing else
+        need_eq = M;
+    } else if (keep > 0) {
+        // Radix select of the keep-th largest key.  With ncand > budget the
+        // answer is a candidate, so only candidates are histogrammed, as
+        // offsets from the smallest; the first pass takes the top 8 bits of
+        // the candidates' own range, spreading them over the 256 bins.
+        // (ncand == 0 keeps one page: the largest key of all.)
+        const bool all = ncand == 0;
+        const uint32_t base = all ? 0u : cmin;
+        const uint32_t span = all ? 0xffffffffu : cmax - cmin;
+        const int nbits = span ? 32 - __builtin_clz(span) : 0;
+        uint32_t prefix = 0;     // determined high bits of (key - base)
+        int remaining = keep;
+        int shift = nbits > 8 ? nbits - 8 : 0;
+        int width = nbits > 8 ? 8 : nbits;
+        while (width > 0) {
+            for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+            const int top = shift + width;
+            const uint32_t hmask = top >= 32 ? 0u : (0xffffffffu << top);
+            const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const uint32_t rel = key[i] - base;
+                if (p0 + i < M && (all || key[i] >= cut) && (rel & hmask) == prefix)
+                    atomicAdd(&hist[(rel >> shift) & dmask], 1);
+            }
+            __syncthreads();
+            if (threadIdx.x < 64) {
+                // Lane l holds digits 255-4l .. 252-4l (descending); the first
+                // lane whose inclusive count reaches `remaining` walks its four.
+                const int l = threadIdx.x;
+                int c4[4], sum = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    c4[i] = hist[255 - 4 * l - i];
+                    sum += c4[i];
+                }
+                const int incl = wave_incl_scan(sum);
+                const uint64_t hit = __ballot(incl >= remaining);
+                const int L = hit ? (int)__builtin_ctzll(hit) : 63;
+                if (l == L) {
+                    int above = incl - sum, dgt = 255 - 4 * l - 3;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (above + c4[i] >= remaining) { dgt = 255 - 4 * l - i; break; }
+                        above += c4[i];
+                    }
+                    sh_digit = dgt;
+                    sh_above = above;
+                }
+            }
+            __syncthreads();
+            prefix |= (uint32_t)sh_digit << shift;
+            remaining -= sh_above;
+            width = shift >= 8 ? 8 : shift;
+            shift -= width;
+        }
+        T = base + prefix;
+        need_eq = remaining;
+    } else {
+        T = 0xffffffffu;
+        need_eq = 0;
+    }
+
+    // Compaction in page order: keys > T, then the first need_eq keys == T.
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (p0 + i < M) {
+            ngt += key[i] > T ? 1 : 0;
+            neq += key[i] == T ? 1 : 0;
+        }
+    }
+    int egt, eeq, tgt, teq;
+    block_excl_scan2<kSelWaves>(ngt, neq, egt, eeq, &tgt, &teq, wsum);
+    int pos = egt + min(eeq, need_eq);
+    int eq_rank = eeq;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (p0 + i < M) {
+            const bool eq = key[i] == T;
+            const bool take = key[i] > T || (eq && eq_rank < need_eq);
+            eq_rank += eq ? 1 : 0;
+            if (take) {
+                if (pos < budget) out[pos] = p0 + i;
+                ++pos;
+            }
+        }
+    }
+    const int written = min(tgt + min(teq, need_eq), budget);
+    for (int i = written + threadIdx.x; i < budget; i += kSelThreads) out[i] = -1;
+    if (threadIdx.x == 0) sel_count[(size_t)b * G + g] = written;
+}
+
+template <int BETA>
+static hipError_t run_gauss_tau(const Dims& d, const float* mu, const float* sigma, const int32_t* seq_lens,
+                                float a, float* tau_hat, hipStream_t s) {
+    // (a*mu, a*sigma) are staged in LDS for sequences of up to kTauLdsPages
+    // pages (64 KiB of the 160 KiB a gfx950 workgroup may use).  The kernel
+    // attribute allowing that much dynamic LDS is set once per device.
+    static bool attr_ok[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    const size_t max_lds = (size_t)kTauLdsPages * sizeof(float2);
+    if (!attr_ok[dev]) {
+        if (hipFuncSetAttribute((const void*)gauss_tau_kernel<BETA>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)max_lds) == hipSuccess)
+            attr_ok[dev] = true;
+        else
+            (void)hipGetLastError();
+    }
+    int lds_pages = attr_ok[dev] ? (d.MP < kTauLdsPages ? d.MP : kTauLdsPages) : 0;
+    if (!attr_ok[dev] && (size_t)d.MP * sizeof(float2) <= 48 * 1024) lds_pages = d.MP;
+    gauss_tau_kernel<BETA><<<dim3(d.HQ, d.B), dim3(kTauThreads), (size_t)lds_pages * sizeof(float2), s>>>(
+        mu, sigma, seq_lens, d.HQ, d.MP, a, lds_pages, tau_hat);
+    return hipGetLastError();
+}
+
 hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
                             const int32_t* seq_lens, float alpha, float* tau_hat, hipStream_t s) {
     const float a = alpha - 1.0f;
-    const int beta = (int)lrintf(1.0f / a);
-    // Stage (a*mu, a*sigma) in LDS for sequences of up to kTauLdsPages pages
-    // (64 KiB; gfx950 gives a workgroup up to 160 KiB of LDS).
-    int lds_pages = d.MP < kTauLdsPages ? d.MP : kTauLdsPages;
-    size_t lds = (size_t)2 * lds_pages * sizeof(float);
-    static bool attr_set[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (lds > 48 * 1024 && !attr_set[dev]) {
-        if (hipFuncSetAttribute((const void*)gauss_tau_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) == hipSuccess) {
-            attr_set[dev] = true;
-        } else {
-            (void)hipGetLastError();
-            lds_pages = 0;
-            lds = 0;
-        }
+    switch ((int)lrintf(1.0f / a)) {
+        case 1: return run_gauss_tau<1>(d, mu, sigma, seq_lens, a, tau_hat, s);
+        case 2: return run_gauss_tau<2>(d, mu, sigma, seq_lens, a, tau_hat, s);
+        case 3: return run_gauss_tau<3>(d, mu, sigma, seq_lens, a, tau_hat, s);
+        default: return hipErrorInvalidValue;
     }
-    gauss_tau_kernel<<<dim3(d.HQ, d.B), dim3(kTauThreads), lds, s>>>(mu, sigma, seq_lens, d.HQ, d.MP,
-                                                                      a, beta, lds_pages, tau_hat);
-    return hipGetLastError();
 }
 
 hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, float alpha,
@@ -295,6 +540,24 @@ hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, floa
                          int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
     const float inv_a = alpha > 1.0f ? 1.0f / (alpha - 1.0f) : 0.0f;
     dim3 grid(d.G, d.B);
+    // Keys in registers when every sequence fits KPT * kSelThreads pages.
+    int kpt = 0;
+    for (int k = 4; k <= 64; k *= 2)
+        if ((long)k * kSelThreads >= d.MP) { kpt = k; break; }
+#define EKV_SELR(RR, GG, KK)                                                                          \
+    select_reg_kernel<GG, RR, KK><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score, \
+                                                                     mu, sigma, tau_hat, inv_a, z,        \
+                                                                     sel_pages, sel_count);               \
+    return hipGetLastError();
+#define EKV_SELK(RR, GG)                                     \
+    switch (kpt) {                                           \
+        case 4: { EKV_SELR(RR, GG, 4) }                      \
+        case 8: { EKV_SELR(RR, GG, 8) }                      \
+        case 16: { EKV_SELR(RR, GG, 16) }                    \
+        case 32: { EKV_SELR(RR, GG, 32) }                    \
+        case 64: { EKV_SELR(RR, GG, 64) }                    \
+        default: break;                                      \
+    }
 #define EKV_SEL(RR, GG)                                                                              \
     select_kernel<GG, RR><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score, mu, \
                                                              sigma, tau_hat, inv_a, z, keys,          \
@@ -302,15 +565,18 @@ hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, floa
     return hipGetLastError();
     if (gauss) {
         switch (d.R) {
-            case 1: { EKV_SEL(1, 1) }
-            case 2: { EKV_SEL(2, 1) }
-            case 4: { EKV_SEL(4, 1) }
-            case 8: { EKV_SEL(8, 1) }
+            case 1: { EKV_SELK(1, 1) EKV_SEL(1, 1) }
+            case 2: { EKV_SELK(2, 1) EKV_SEL(2, 1) }
+            case 4: { EKV_SELK(4, 1) EKV_SEL(4, 1) }
+            case 8: { EKV_SELK(8, 1) EKV_SEL(8, 1) }
             default: return hipErrorInvalidValue;
         }
     }
+    EKV_SELK(1, 0)
     EKV_SEL(1, 0)
 #undef EKV_SEL
+#undef EKV_SELK
+#undef EKV_SELR
 }
 
 }  // namespace ekv

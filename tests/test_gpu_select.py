@@ -1,0 +1,128 @@
+"""GPU parity of ekv_select on its own, against the fp64 oracle, at page
+counts that reach every kernel variant (keys in registers at 4..64 keys per
+thread, and the global-memory path beyond 65536 pages), with ragged and empty
+sequences and exact ties.  Selection rules: "EntmaxKV: Support-Aware Decoding
+for Entmax Attention" section 4.3 (top-k page selection; Gaussian-aware
+selection with the threshold of Appendix C.2 Eq. (18)); the Gaussian page rule
+is this library's reading of the lost Eq. (21)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_long_context_ekv_amd import ekv
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+P = 16
+
+
+def _shape(B, G, R, MP):
+    return ekv.make_shape(B, G * R, G, 128, MP, 1, "bf16", "f32")
+
+
+def _run_select(sh, selector, lens, alpha, budget, z, score=None, mu=None, sigma=None):
+    B, G, HQ = sh.batch, sh.num_kv_groups, sh.num_q_heads
+    sel = torch.full((B, G, budget), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    th = torch.full((B, HQ), 7.0, device="cuda") if selector == ekv.SEL_GAUSS else None
+    ws = torch.empty(ekv.select_workspace_bytes(sh, selector, alpha, budget, z), dtype=torch.uint8, device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ekv.select(sh, selector, sl, alpha, budget, z, score, mu, sigma, sel, cnt, th, ws)
+    H.sync()
+    return sel.cpu().numpy(), cnt.cpu().numpy(), (None if th is None else th.cpu().numpy().astype(np.float64))
+
+
+def _check_rows(sel, cnt, b, g, want, keys, budget):
+    c = int(cnt[b, g])
+    row = sel[b, g]
+    assert c == len(want), (b, g, c, len(want))
+    assert np.all(row[c:] == -1)
+    assert np.all(np.diff(row[:c]) > 0)
+    return H.compare_selection(row[:c], want, keys, len(want))
+
+
+@pytest.mark.parametrize("MP", [300, 5000, 9000, 20000, 40000, 65536, 70000])
+def test_topk_select_sizes(MP):
+    print(f"[case] topk MP={MP}", flush=True)
+    B, G, budget = 3, 2, 128
+    lens = [MP * P, (MP // 2) * P + 5, 37]
+    rng = np.random.default_rng(MP)
+    score = rng.standard_normal((B, G, MP)).astype(np.float32)
+    sel, cnt, _ = _run_select(_shape(B, G, 1, MP), ekv.SEL_TOPK, lens, 1.5, budget, 3.0,
+                              score=torch.from_numpy(score).cuda())
+    for b in range(B):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            U = score[b, g, :M].astype(np.float64)
+            want = oracle.select.topk_pages(U, budget)
+            _check_rows(sel, cnt, b, g, want, U, budget)
+
+
+@pytest.mark.parametrize("MP", [3000, 20000, 70000])
+def test_topk_select_exact_ties(MP):
+    """Integer-valued scores: many exact ties, broken toward the lower page
+    index; fp32 and fp64 agree exactly, so the selection must be identical."""
+    print(f"[case] ties MP={MP}", flush=True)
+    B, G, budget = 2, 2, 200
+    lens = [MP * P, MP * P - 3]
+    rng = np.random.default_rng(7 + MP)
+    score = rng.integers(-20, 21, size=(B, G, MP)).astype(np.float32)
+    sel, cnt, _ = _run_select(_shape(B, G, 1, MP), ekv.SEL_TOPK, lens, 1.5, budget, 3.0,
+                              score=torch.from_numpy(score).cuda())
+    for b in range(B):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            want = oracle.select.topk_pages(score[b, g, :M].astype(np.float64), budget)
+            c = int(cnt[b, g])
+            np.testing.assert_array_equal(sel[b, g, :c], want)
+
+
+def test_topk_select_empty_and_short():
+    B, G, budget, MP = 3, 2, 64, 100
+    lens = [0, 40 * P - 1, 100 * P]
+    score = torch.randn(B, G, MP, generator=torch.Generator().manual_seed(3)).cuda()
+    sel, cnt, _ = _run_select(_shape(B, G, 1, MP), ekv.SEL_TOPK, lens, 1.5, budget, 3.0, score=score)
+    assert np.all(cnt[0] == 0) and np.all(sel[0] == -1)
+    for g in range(G):
+        assert cnt[1, g] == 40
+        np.testing.assert_array_equal(sel[1, g, :40], np.arange(40))
+        assert np.all(sel[1, g, 40:] == -1)
+        assert cnt[2, g] == budget
+
+
+@pytest.mark.parametrize("MP,alpha", [(600, 1.5), (8192, 1.5), (8192, 2.0), (8192, 4.0 / 3.0), (20000, 1.5),
+                                      (70000, 1.5)])
+def test_gauss_select_sizes(MP, alpha):
+    """tau_hat against the oracle's fp64 Eq. (18) root; the page rule
+    against the oracle's margins computed from the GPU's own tau_hat."""
+    print(f"[case] gauss MP={MP} alpha={alpha}", flush=True)
+    B, G, R, budget, z = 2, 2, 4, 256, 3.0
+    lens = [MP * P - 9, (MP // 3) * P]
+    rng = np.random.default_rng(MP + int(alpha * 10))
+    mu = (rng.standard_normal((B, G * R, MP)) * 0.25).astype(np.float32)
+    sg = (0.8 + 0.4 * rng.random((B, G * R, MP))).astype(np.float32)
+    sg[:, :, ::97] = 0.0                      # some zero-variance pages
+    sel, cnt, th = _run_select(_shape(B, G, R, MP), ekv.SEL_GAUSS, lens, alpha, budget, z,
+                               mu=torch.from_numpy(mu).cuda(), sigma=torch.from_numpy(sg).cuda())
+    for b in range(B):
+        n = lens[b]
+        M = (n + P - 1) // P
+        n_p = oracle.paged.page_valid_counts(n, P)
+        for h in range(G * R):
+            m64, s64 = mu[b, h, :M].astype(np.float64), sg[b, h, :M].astype(np.float64)
+            want = oracle.select.gauss_tau_hat(m64, s64, n_p, alpha)
+            assert H.tau_close(th[b, h], want), (b, h, th[b, h], want)
+        for g in range(G):
+            hs = slice(g * R, (g + 1) * R)
+            m64, s64 = mu[b, hs, :M].astype(np.float64), sg[b, hs, :M].astype(np.float64)
+            t = oracle.select.gauss_margins(m64, s64, th[b, hs], alpha)
+            want = oracle.select.gauss_select(m64, s64, th[b, hs], alpha, z, budget)
+            c = int(cnt[b, g])
+            row = sel[b, g]
+            assert c == len(want) or np.any(np.abs(t + z) < 1e-4 * z)
+            assert np.all(row[c:] == -1) and np.all(np.diff(row[:c]) > 0)
+            if c == len(want):
+                H.compare_selection(row[:c], want, t, len(want))
