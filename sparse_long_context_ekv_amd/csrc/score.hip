@@ -14,8 +14,11 @@
 // Both kernels are pure streams over the page statistics: one 16-lane row
 // per (page, group), lane l owning channels [l*CH, (l+1)*CH), the r query
 // slices of the group in registers, one fixed-order DPP row sum per head.
-// A block covers `ppb` consecutive logical pages of one sequence; each row
-// issues the loads of UNROLL pages before using any of them.
+// A block covers 2^lg_ppb consecutive logical pages of one sequence; each row
+// issues the loads of UNROLL pages before using any of them.  Results are
+// staged in LDS and written once per block, one contiguous run of pages per
+// output row: single-float stores scattered over the [B][.][MP] rows (one per
+// page and head) cost more HBM time than the whole statistics stream saves.
 #include "ekv_device.h"
 #include "ekv_internal.h"
 
@@ -27,18 +30,20 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void box_score_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const T* __restrict__ kmin, const T* __restrict__ kmax,
-    float* __restrict__ score, int G, int MP, int NP, int ppb, float inv_sqrt_d) {
+    float* __restrict__ score, int G, int MP, int NP, int lg_ppb, float inv_sqrt_d) {
     constexpr int CH = D / kRow;
+    extern __shared__ float stage[];           // [G][ppb]
+    const int ppb = 1 << lg_ppb;
     const int b = blockIdx.y;
     const int M = num_pages(seq_len_at(seq_lens, b, MP));
     const int p_begin = blockIdx.x * ppb;
-    if (p_begin >= M) return;
+    if (p_begin >= M) return;                  // block-uniform
     const int p_end = min(M, p_begin + ppb);
     const int lane = threadIdx.x & (kRow - 1);
     const int row = threadIdx.x >> 4;
     const int per_iter = kRow / G;
-    if (row >= per_iter * G) return;
-    const int slot = row / G, g = row % G;
+    const bool active = row < per_iter * G;    // idle rows still reach the barrier
+    const int slot = row / G, g = active ? row % G : 0;
     const int HQ = G * R;
 
     Vec<T, CH> qv[R];
@@ -62,8 +67,7 @@ __global__ __launch_bounds__(256) void box_score_kernel(
     (void)pick_max;
 
     const int32_t* pt = page_table + (size_t)b * MP;
-    float* out = score + ((size_t)b * G + g) * MP;
-    for (int p0 = p_begin + slot; p0 < p_end; p0 += kUnroll * per_iter) {
+    for (int p0 = p_begin + slot; active && p0 < p_end; p0 += kUnroll * per_iter) {
         Vec<T, CH> lo[kUnroll], hi[kUnroll];
         bool ok[kUnroll];
 #pragma unroll
@@ -102,8 +106,14 @@ __global__ __launch_bounds__(256) void box_score_kernel(
                 }
                 best = fmaxf(best, row_sum16(acc));
             }
-            if (lane == 0) out[p0 + u * per_iter] = best * inv_sqrt_d;
+            if (lane == 0) stage[(g << lg_ppb) + p0 + u * per_iter - p_begin] = best * inv_sqrt_d;
         }
+    }
+    __syncthreads();
+    const int np = p_end - p_begin;
+    for (int i = threadIdx.x; i < (G << lg_ppb); i += blockDim.x) {
+        const int gg = i >> lg_ppb, pp = i & (ppb - 1);
+        if (pp < np) score[((size_t)b * G + gg) * MP + p_begin + pp] = stage[i];
     }
 }
 
@@ -111,19 +121,21 @@ template <typename T, typename S, int D, int R>
 __global__ __launch_bounds__(256) void gauss_score_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const S* __restrict__ kmean, const S* __restrict__ kvar,
-    float* __restrict__ mu, float* __restrict__ sigma, int G, int MP, int NP, int ppb,
+    float* __restrict__ mu, float* __restrict__ sigma, int G, int MP, int NP, int lg_ppb,
     float inv_sqrt_d, float inv_d) {
     constexpr int CH = D / kRow;
+    extern __shared__ float stage[];           // [2][HQ][ppb]: mu, then sigma
+    const int ppb = 1 << lg_ppb;
     const int b = blockIdx.y;
     const int M = num_pages(seq_len_at(seq_lens, b, MP));
     const int p_begin = blockIdx.x * ppb;
-    if (p_begin >= M) return;
+    if (p_begin >= M) return;                  // block-uniform
     const int p_end = min(M, p_begin + ppb);
     const int lane = threadIdx.x & (kRow - 1);
     const int row = threadIdx.x >> 4;
     const int per_iter = kRow / G;
-    if (row >= per_iter * G) return;
-    const int slot = row / G, g = row % G;
+    const bool active = row < per_iter * G;    // idle rows still reach the barrier
+    const int slot = row / G, g = active ? row % G : 0;
     const int HQ = G * R;
 
     float qf[R][CH], q2[R][CH];
@@ -139,11 +151,11 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
     }
 
     const int32_t* pt = page_table + (size_t)b * MP;
-    // lane j < R writes mu of head g*R+j, lane R+j writes its sigma
+    // lane j < R holds mu of head g*R+j, lane R+j its sigma
     const int jh = lane < R ? lane : lane - R;
-    float* dst = (lane < R ? mu : sigma) + ((size_t)b * HQ + g * R + jh) * MP;
+    float* dst = stage + ((lane < R ? 0 : HQ) + g * R + jh) * ppb;
     const bool writer = lane < 2 * R;
-    for (int p0 = p_begin + slot; p0 < p_end; p0 += kUnroll * per_iter) {
+    for (int p0 = p_begin + slot; active && p0 < p_end; p0 += kUnroll * per_iter) {
         Vec<S, CH> mv[kUnroll], vv[kUnroll];
         bool ok[kUnroll];
 #pragma unroll
@@ -174,37 +186,47 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
                 mine = (lane == j) ? am * inv_sqrt_d : mine;
                 mine = (lane == R + j) ? sqrtf(fmaxf(av, 0.0f) * inv_d) : mine;
             }
-            if (writer) dst[p0 + u * per_iter] = mine;
+            if (writer) dst[p0 + u * per_iter - p_begin] = mine;
         }
+    }
+    __syncthreads();
+    const int np = p_end - p_begin;
+    for (int i = threadIdx.x; i < (2 * HQ) << lg_ppb; i += blockDim.x) {
+        const int hh = i >> lg_ppb, pp = i & (ppb - 1);
+        float* o = hh < HQ ? mu + ((size_t)b * HQ + hh) * MP : sigma + ((size_t)b * HQ + hh - HQ) * MP;
+        if (pp < np) o[p_begin + pp] = stage[i];
     }
 }
 
-static int score_ppb(const Dims& d) {
-    // Enough blocks to fill 256 CUs several times over, at most 256 pages each.
-    long units = (long)d.B * d.MP;
-    int ppb = 64;
-    while (ppb > 8 && units / ppb < 4096) ppb >>= 1;
-    return ppb;
+// log2 of the pages per block: 16 (measured best on the 128K batched
+// workload), fewer when that leaves under ~2048 blocks for 256 CUs.
+static int score_lg_ppb(const Dims& d) {
+    const long units = (long)d.B * d.MP;
+    int lg = 4;
+    while (lg > 2 && (units >> lg) < 2048) --lg;
+    return lg;
 }
 
 template <typename T, int D, int R>
 static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                           const void* kmin, const void* kmax, float* score, hipStream_t s) {
-    const int ppb = score_ppb(d);
-    dim3 grid((d.MP + ppb - 1) / ppb, d.B);
-    box_score_kernel<T, D, R><<<grid, dim3(256), 0, s>>>((const T*)q, pt, sl, (const T*)kmin, (const T*)kmax,
-                                                         score, d.G, d.MP, d.NP, ppb, 1.0f / sqrtf((float)D));
+    const int lg = score_lg_ppb(d);
+    dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
+    const size_t lds = ((size_t)d.G << lg) * sizeof(float);
+    box_score_kernel<T, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const T*)kmin, (const T*)kmax,
+                                                           score, d.G, d.MP, d.NP, lg, 1.0f / sqrtf((float)D));
     return hipGetLastError();
 }
 
 template <typename T, typename S, int D, int R>
 static hipError_t run_gauss(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                             const void* kmean, const void* kvar, float* mu, float* sigma, hipStream_t s) {
-    const int ppb = score_ppb(d);
-    dim3 grid((d.MP + ppb - 1) / ppb, d.B);
-    gauss_score_kernel<T, S, D, R><<<grid, dim3(256), 0, s>>>((const T*)q, pt, sl, (const S*)kmean, (const S*)kvar,
-                                                              mu, sigma, d.G, d.MP, d.NP, ppb,
-                                                              1.0f / sqrtf((float)D), 1.0f / (float)D);
+    const int lg = score_lg_ppb(d);
+    dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
+    const size_t lds = ((size_t)2 * d.HQ << lg) * sizeof(float);
+    gauss_score_kernel<T, S, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const S*)kmean,
+                                                                (const S*)kvar, mu, sigma, d.G, d.MP, d.NP, lg,
+                                                                1.0f / sqrtf((float)D), 1.0f / (float)D);
     return hipGetLastError();
 }
 
