@@ -175,7 +175,7 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
     if (sparse && sel_stride < 1) return fail(EKV_ERR_INVALID_ARG, "sel_stride=%d < 1", sel_stride);
     if (sparse && !sel_count) return fail(EKV_ERR_INVALID_ARG, "sel_count is required with sel_pages");
     if (delta && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "delta needs tau_ref");
-    const ekv::DecodePlan pl = ekv::plan_decode(d, sparse, sparse ? sel_stride : 0);
+    const ekv::DecodePlan pl = ekv::plan_decode(d, sparse, sparse ? sel_stride : 0, alpha);
     if (!workspace) {
         *workspace_bytes = pl.bytes;
         return ok();

@@ -36,15 +36,19 @@ constexpr int kLogitUnroll = 4;
 constexpr int kCandCap = 8192;
 
 // -------------------------------------------------------------- logits ----
-template <typename T, int D, int R>
+// PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
+// which the general threshold kernel reads (softmax, full cache).
+template <typename T, int D, int R, bool PART>
 __global__ __launch_bounds__(256) void logits_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int ppb,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int lg_ppb,
     int nslot, int nchunk1, float inv_sqrt_d, float* __restrict__ logits, float* __restrict__ part1) {
     constexpr int CH = D / kRow;
     constexpr int NW = Vec<T, CH>::NW;
+    extern __shared__ float stage[];           // [R][ppb * kPage] logits of this chunk
     __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
+    const int ppb = 1 << lg_ppb;
     const int unit = blockIdx.y;
     const int b = unit / G, g = unit - b * G;
     const int HQ = G * R;
@@ -60,8 +64,7 @@ __global__ __launch_bounds__(256) void logits_kernel(
 #pragma unroll
     for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
 
-    const int hj = lane < R ? lane : 0;        // head owned by this lane (lanes < R)
-    float* lrow = logits + ((size_t)b * HQ + g * R + hj) * nslot;
+    float* st = stage + ((lane < R ? lane : 0) << (lg_ppb + 4)) + row;   // lane j < R: head j
     float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
     const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
 
@@ -103,8 +106,8 @@ __global__ __launch_bounds__(256) void logits_kernel(
                 if (lp[u] * kPage + row >= n) mine = -INFINITY;   // past the sequence end
             }
             if (lane < R) {
-                lrow[(size_t)ii * kPage + row] = mine;
-                if (mine > -INFINITY) {
+                st[(ii - i0) * kPage] = mine;
+                if (PART && mine > -INFINITY) {
                     if (mine > run_m) {
                         run_l = run_l * expf(run_m - mine) + 1.0f;
                         run_m = mine;
@@ -116,13 +119,20 @@ __global__ __launch_bounds__(256) void logits_kernel(
             }
         }
     }
-    if (lane < R) {
+    if (PART && lane < R) {
         sh_m[row][lane] = run_m;
         sh_l[row][lane] = run_l;
         sh_c[row][lane] = run_c;
     }
     __syncthreads();
-    if (threadIdx.x < R) {
+    // One contiguous run of (i1 - i0) * 16 slots per head.
+    const int nsl = max(i1 - i0, 0) * kPage;
+    const int per_head = ppb * kPage;
+    for (int t = threadIdx.x; t < R * per_head; t += blockDim.x) {
+        const int j = t >> (lg_ppb + 4), r = t & (per_head - 1);
+        if (r < nsl) logits[((size_t)b * HQ + g * R + j) * nslot + i0 * kPage + r] = stage[t];
+    }
+    if (PART && threadIdx.x < R) {
         const int j = threadIdx.x;
         float m = -INFINITY;
         for (int r2 = 0; r2 < kRow; ++r2) m = fmaxf(m, sh_m[r2][j]);
@@ -446,15 +456,334 @@ __global__ void reduce_kernel(const float* __restrict__ part3, int HQ, int D, in
     }
 }
 
+// ------------------------------------------------- fused tau + PV (sparse) ----
+constexpr int kFusedMaxSlots = 4096;   // selected slots per head on the fused path
+constexpr int kCandLds = 1024;         // threshold candidates per head kept in LDS
+constexpr int kPvList = 512;           // support entries per PV pass
+
+// Orders this wave's LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wave-wide sum of an int (any order is exact).
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int MODE>
+__device__ __forceinline__ float pw(float d, float beta) {      // d^beta, d > 0
+    return MODE == kModeBeta1 ? d : (MODE == kModeBeta2 ? d * d : powf(d, beta));
+}
+template <int MODE>
+__device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d > 0
+    return MODE == kModeBeta1 ? 1.0f : (MODE == kModeBeta2 ? d : powf(d, beta - 1.0f));
+}
+
+// One block per (sequence, KV group) with one wave per query head of the
+// group; the waves never synchronise with each other.  Wave j:
+//  0. stages the physical page of every selected page in LDS (its loads
+//     overlap the logits loads);
+//  1. holds x = (alpha-1) s of its head's selected slots in registers
+//     (slot k*256 + 4*lane + c in xr[k][c]), invalid slots -inf;
+//  2. compacts the threshold candidates x > max(x) - 1 (only those can be in
+//     the support: the top term alone is at most 1) with their slots into
+//     LDS, lane by lane after one wave scan of per-lane counts (a fixed
+//     order, so results are reproducible); past kCandLds candidates it keeps
+//     working on the registers;
+//  3. finds tau from sum [x - tau]_+^beta = 1 by Newton steps on
+//     F^(1/beta) from tau = max(x) - 1: for beta >= 1 this is the L^beta norm
+//     of (x - tau)_+, convex and decreasing, so the steps rise monotonically
+//     without passing the root (beta < 1: bisection); for beta in {1, 2} the
+//     closed form on the support found then gives tau exactly;
+//  4. writes tau, the support size and the dropped mass w.r.t. tau_ref
+//     (tau_ref, the threshold over a superset of these tokens, is at least
+//     max(x) - 1, so only candidates contribute);
+//  5. compacts its support (slot, p = [x - tau]_+^beta) and gathers only
+//     those V rows, four per step across the 16-lane rows, summing p v in a
+//     fixed order.
+template <typename T, int D, int R, int KPL, int MODE>
+__global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
+    const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
+    int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
+    float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
+    float* __restrict__ delta_out) {
+    constexpr int CH = D / kRow;
+    constexpr int PVU = 4;                       // V rows per 16-lane row in flight
+    constexpr int NPG = KPL * 256 / kPage;       // selected pages per head at most
+    __shared__ float cand_x[R][kCandLds + 64];   // + one dump slot per lane
+    __shared__ int cand_s[R][kCandLds + 64];
+    __shared__ int pv_slot[R][kPvList + 64];
+    __shared__ float pv_p[R][kPvList + 64];
+    __shared__ int phys_of[R][NPG];
+    const int unit = blockIdx.x;
+    const int b = unit / G, g = unit - b * G;
+    const int HQ = G * R;
+    const int j = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const size_t oh = (size_t)b * HQ + g * R + j;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = min(max(sel_count[unit], 0), min(sel_stride, NPG));
+    const int nused = cnt * kPage;
+    const size_t nslot = (size_t)sel_stride * kPage;
+    const float a = alpha - 1.0f;
+    const float* lrow = logits + oh * nslot;
+    float* o = out + oh * D;
+
+    // 0. selected logical pages (loads issued first), then the logits
+    const int32_t* sel = sel_pages + (size_t)unit * sel_stride;
+    constexpr int NPL = (NPG + 63) / 64;
+    int lpg[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int ip = i * 64 + lane;
+        lpg[i] = ip < cnt ? sel[ip] : -1;
+    }
+    float xr[KPL][4];
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+        const int s0 = k * 256 + 4 * lane;
+        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (s0 < nused) v = *reinterpret_cast<const float4*>(lrow + s0);
+        xr[k][0] = v.x;
+        xr[k][1] = v.y;
+        xr[k][2] = v.z;
+        xr[k][3] = v.w;
+    }
+    const int32_t* pt = page_table + (size_t)b * MP;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int ip = i * 64 + lane;
+        if (ip < NPG) {
+            const int lp = lpg[i];
+            const int ph = (lp >= 0 && lp < M) ? pt[lp] : -1;
+            phys_of[j][ip] = (ph >= 0 && ph < NP) ? ph : -1;
+        }
+    }
+
+    float xmax = -INFINITY;
+    int nvalid = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xr[k][c] *= a;
+            xmax = fmaxf(xmax, xr[k][c]);
+            nvalid += xr[k][c] > -INFINITY ? 1 : 0;
+        }
+    xmax = wave_max(xmax);
+    if (!(xmax > -INFINITY)) {                   // empty candidate set (wave-uniform)
+        for (int c = lane; c < D; c += 64) o[c] = 0.0f;
+        if (lane == 0) {
+            tau_out[oh] = -INFINITY;
+            if (support_out) support_out[oh] = 0;
+            if (delta_out) delta_out[oh] = 1.0f;
+        }
+        return;
+    }
+    nvalid = wave_isum(nvalid);
+    const float lo = xmax - 1.0f;
+
+    // 2. candidates x > lo
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mine += xr[k][c] > lo ? 1 : 0;
+    const int incl = wave_incl_scan(mine);
+    const int ncand = __shfl(incl, 63, 64);
+    const bool in_lds = ncand <= kCandLds;
+    float* cx = cand_x[j];
+    int* cs = cand_s[j];
+    if (in_lds) {
+        int pos = incl - mine;
+        const int dump = kCandLds + lane;
+#pragma unroll
+        for (int k = 0; k < KPL; ++k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool f = xr[k][c] > lo;
+                const int at = f ? pos : dump;
+                cx[at] = xr[k][c];
+                cs[at] = k * 256 + 4 * lane + c;
+                pos += f ? 1 : 0;
+            }
+        wave_lds_sync();
+    }
+    // Visit every candidate (x, slot) this lane owns.
+    auto each_cand = [&](auto&& fn) {
+        if (in_lds) {
+            for (int i = lane; i < ncand; i += 64) fn(cx[i], cs[i]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < KPL; ++k)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (xr[k][c] > lo) fn(xr[k][c], k * 256 + 4 * lane + c);
+        }
+    };
+
+    // 3. tau
+    auto sums = [&](float t, float& f, float& df) {
+        float s1 = 0.0f, s0 = 0.0f;
+        each_cand([&](float x, int) {
+            const float d = x - t;
+            if (d > 0.0f) {
+                s1 += pw<MODE>(d, beta);
+                s0 += pw1<MODE>(d, beta);
+            }
+        });
+        f = wave_sum(s1);
+        df = wave_sum(s0);
+    };
+    float tau = lo;
+    if (MODE != kModeGeneral || beta >= 1.0f) {
+        for (int it = 0; it < 100; ++it) {
+            float f, df;
+            sums(tau, f, df);
+            if (!(f > 1.0f) || !(df > 0.0f)) break;
+            const float gr = MODE == kModeBeta1 ? f : (MODE == kModeBeta2 ? sqrtf(f) : powf(f, 1.0f / beta));
+            const float nt = tau + (1.0f - 1.0f / gr) * f / df;
+            if (!(nt > tau)) break;
+            tau = nt;
+        }
+    } else {
+        // beta < 1 (alpha > 2): bisection on [max - 1, max - n^(1-alpha)]
+        float l2 = lo, hi = xmax - powf((float)nvalid, 1.0f - alpha);
+        for (int it = 0; it < 60; ++it) {
+            const float mid = 0.5f * (l2 + hi);
+            float f, df;
+            sums(mid, f, df);
+            if (f >= 1.0f) l2 = mid; else hi = mid;
+        }
+        tau = 0.5f * (l2 + hi);
+    }
+    // Closed form on the support found (beta in {1, 2}), kept if consistent.
+    if constexpr (MODE == kModeBeta1 || MODE == kModeBeta2) {
+        float sx = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
+        each_cand([&](float x, int) {
+            if (x > tau) { sx += x; kk += 1.0f; mn = fminf(mn, x); }
+            else rest = fmaxf(rest, x);
+        });
+        sx = wave_sum(sx);
+        kk = wave_sum(kk);
+        mn = -wave_max(-mn);
+        rest = wave_max(rest);
+        float tcf = NAN;
+        if (kk > 0.0f) {
+            if constexpr (MODE == kModeBeta1) {
+                tcf = (sx - 1.0f) / kk;
+            } else {
+                const float mean = sx / kk;
+                float v = 0.0f;
+                each_cand([&](float x, int) {
+                    if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
+                });
+                v = wave_sum(v);
+                if (v <= 1.0f) tcf = mean - sqrtf((1.0f - v) / kk);
+            }
+        }
+        if (tcf == tcf && mn > tcf && !(rest > tcf)) tau = tcf;
+    }
+
+    // 4. support size and dropped mass with respect to tau_ref
+    int ns = 0;
+    float kept = 0.0f;
+    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+    each_cand([&](float x, int) {
+        ns += x > tau ? 1 : 0;
+        if (delta_out && x > tref) kept += pw<MODE>(x - tref, beta);
+    });
+    const int sinc = wave_incl_scan(ns);
+    const int nsup = __shfl(sinc, 63, 64);
+    if (delta_out) kept = wave_sum(kept);
+    if (lane == 0) {
+        tau_out[oh] = tau;
+        if (support_out) support_out[oh] = nsup;
+        if (delta_out) delta_out[oh] = 1.0f - kept;
+    }
+
+    // 5. PV over the support, in passes of kPvList entries.
+    const int rg = lane >> 4, l16 = lane & (kRow - 1);
+    int* ls = pv_slot[j];
+    float* lpv = pv_p[j];
+    const int* phl = phys_of[j];
+    float acc[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+    for (int start = 0; start < nsup; start += kPvList) {
+        if (start > 0) wave_lds_sync();          // the previous pass has read its list
+        int pos = sinc - ns - start;
+        const int dump = kPvList + lane;
+        each_cand([&](float x, int slot) {
+            if (x > tau) {
+                const int at = (pos >= 0 && pos < kPvList) ? pos : dump;
+                ls[at] = slot;
+                lpv[at] = pw<MODE>(x - tau, beta);
+                ++pos;
+            }
+        });
+        wave_lds_sync();
+        const int nent = min(nsup - start, kPvList);
+        for (int e0 = 0; e0 < nent; e0 += 4 * PVU) {
+            Vec<T, CH> vv[PVU];
+            float pp[PVU];
+            bool okv[PVU];
+#pragma unroll
+            for (int u = 0; u < PVU; ++u) {
+                const int e = e0 + 4 * u + rg;
+                okv[u] = false;
+                pp[u] = 0.0f;
+                if (e < nent) {
+                    const int slot = ls[e];
+                    const int phys = phl[slot >> 4];
+                    if (phys >= 0) {
+                        okv[u] = true;
+                        pp[u] = lpv[e];
+                        vv[u].load(v_cache + (((size_t)phys * G + g) * kPage + (slot & (kPage - 1))) * D + l16 * CH);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < PVU; ++u)
+                if (okv[u])
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) acc[c] = fmaf(pp[u], vv[u].get(c), acc[c]);
+        }
+    }
+    // Fixed-order sum of the four 16-lane rows; lanes 0..15 write.
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        float v = acc[c];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[c] = v;
+    }
+    if (lane < kRow) {
+#pragma unroll
+        for (int c = 0; c < CH; c += 4)
+            *reinterpret_cast<float4*>(o + l16 * CH + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+    }
+}
+
 // ---------------------------------------------------------------- host ----
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride) {
+DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     DecodePlan pl;
     pl.sparse = sparse;
     const int maxp = sparse ? sel_stride : d.MP;
     pl.nslot = maxp * kPage;
-    pl.ppb = sparse ? 8 : 32;
+    pl.fused = sparse && alpha > 1.0f && pl.nslot <= kFusedMaxSlots;
+    pl.lg_ppb = sparse ? 3 : 5;
+    pl.ppb = 1 << pl.lg_ppb;
     pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
     if (pl.nchunk1 < 1) pl.nchunk1 = 1;
     pl.spb = sparse ? 256 : 4096;
@@ -463,9 +792,33 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride) {
     const size_t bh = (size_t)d.B * d.HQ;
     pl.off_logits = 0;
     pl.off_part1 = align256(bh * pl.nslot * sizeof(float));
-    pl.off_part3 = pl.off_part1 + align256(bh * pl.nchunk1 * 3 * sizeof(float));
-    pl.bytes = pl.off_part3 + align256(bh * pl.nchunk3 * d.D * sizeof(float));
+    if (pl.fused) {
+        pl.off_part3 = pl.off_part1;
+        pl.bytes = pl.off_part1;
+    } else {
+        pl.off_part3 = pl.off_part1 + align256(bh * pl.nchunk1 * 3 * sizeof(float));
+        pl.bytes = pl.off_part3 + align256(bh * pl.nchunk3 * d.D * sizeof(float));
+    }
     return pl;
+}
+
+template <typename T, int D, int R, int MODE>
+static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_cache, const int32_t* pt,
+                            const int32_t* sl, const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
+                            float alpha, float beta, const float* logits, const float* tau_ref, float* out,
+                            float* tau, int32_t* support, float* delta, hipStream_t s) {
+    const int units = d.B * d.G;
+#define EKV_FUSED(KK)                                                                                      \
+    sparse_tau_pv_kernel<T, D, R, KK, MODE><<<dim3(units), dim3(64 * R), 0, s>>>(                          \
+        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
+        tau_ref, out, tau, support, delta);                                                                \
+    return hipGetLastError();
+    if (pl.nslot <= 256) { EKV_FUSED(1) }
+    if (pl.nslot <= 512) { EKV_FUSED(2) }
+    if (pl.nslot <= 1024) { EKV_FUSED(4) }
+    if (pl.nslot <= 2048) { EKV_FUSED(8) }
+    EKV_FUSED(16)
+#undef EKV_FUSED
 }
 
 template <typename T, int D, int R>
@@ -478,9 +831,29 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
     float* part1 = (float*)(ws + pl.off_part1);
     float* part3 = (float*)(ws + pl.off_part3);
     const int units = d.B * d.G;
-    logits_kernel<T, D, R><<<dim3(pl.nchunk1, units), dim3(256), 0, s>>>(
+    const size_t lds = ((size_t)R * pl.ppb * kPage) * sizeof(float);
+    if (pl.fused) {
+        logits_kernel<T, D, R, false><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
+            (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
+            pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        switch (mode) {
+            case kModeBeta1:
+                return run_fused<T, D, R, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, s);
+            case kModeBeta2:
+                return run_fused<T, D, R, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, s);
+            default:
+                return run_fused<T, D, R, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,
+                                                        sel_stride, alpha, beta, logits, tau_ref, out, tau,
+                                                        support, delta, s);
+        }
+    }
+    logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
         (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
-        pl.ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
+        pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,

@@ -178,6 +178,31 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red, int& 
     b = sb;
 }
 
+// Three block-uniform sums with one barrier.  `red` holds at least 6*NW floats.
+template <int NW>
+__device__ __forceinline__ void block_sum3(float& a, float& b, float& c, float* red, int& phase) {
+    const float wa = wave_sum(a), wb = wave_sum(b), wc = wave_sum(c);
+    const int wid = threadIdx.x >> 6;
+    float* r = red + phase * 3 * NW;
+    if ((threadIdx.x & 63) == 0) {
+        r[wid] = wa;
+        r[NW + wid] = wb;
+        r[2 * NW + wid] = wc;
+    }
+    __syncthreads();
+    float sa = r[0], sb = r[NW], sc = r[2 * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        sa += r[i];
+        sb += r[NW + i];
+        sc += r[2 * NW + i];
+    }
+    phase ^= 1;
+    a = sa;
+    b = sb;
+    c = sc;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele on
 // shuffles; integer, so the order does not matter).
 __device__ __forceinline__ int wave_incl_scan(int v) {

@@ -39,6 +39,8 @@ hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, floa
 // Decode.
 struct DecodePlan {
     int sparse;      // selection given
+    int fused;       // sparse entmax: logits kernel + one tau/PV kernel per (b, g)
+    int lg_ppb;      // log2 of ppb
     int nslot;       // logits slots per (b, h)
     int ppb;         // pages per logits block
     int nchunk1;     // logits blocks per (b, g)
@@ -46,7 +48,7 @@ struct DecodePlan {
     int nchunk3;     // PV blocks per (b, g)
     size_t off_logits, off_part1, off_part3, bytes;
 };
-DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride);
+DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha);
 hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,

@@ -34,6 +34,9 @@ constexpr int kTauWaves = kTauThreads / 64;
 constexpr int kTauLdsPages = 8192;     // 64 KiB of LDS for the (a*mu, a*sigma) pairs
 constexpr int kTauMaxIter = 40;
 constexpr float kTauTol = 1e-5f;       // stop once a step is below this (relative)
+constexpr int kTauSub = 16;            // warm start: every 16th page ...
+constexpr int kTauSubMin = 2048;       // ... for sequences of at least this many pages
+constexpr float kTauSubTol = 1e-4f;
 
 // Standard normal upper tail Q(x) = 1 - Phi(x), x >= 0, as phi(x) R(x) with
 // the Mills ratio R(x) ~ t h(t), t = 1/(1 + kMillsK x), h the polynomial
@@ -47,15 +50,18 @@ constexpr float kMillsC[12] = {
 constexpr float kTinyV = 1e-30f;       // v at or below this: the page is a point mass
 
 // n_p-free terms of page p at threshold tau, with m = (alpha-1) mu_p - tau,
-// v = (alpha-1) sigma_p, z = m/v: e_b = E[Y_+^beta], e_bm1 = E[Y_+^(beta-1)]
-// for Y ~ N(m, v^2) (E[Y_+^0] = P(Y > 0) = Phi(z)).  A page with v <= kTinyV
-// is a point mass at m: E[Y_+^k] = [m]_+^k.  Branch-free: both forms are
-// computed and one is selected.
+// v = (alpha-1) sigma_p, z = m/v: e_b = E[Y_+^beta], e_b1 = E[Y_+^(beta-1)],
+// e_b2 = E[Y_+^(beta-2)] for Y ~ N(m, v^2), where E[Y_+^0] = P(Y > 0) = Phi(z)
+// and E[Y_+^-1] stands for the density of Y at 0, phi(z)/v (the derivative of
+// Phi(z) in m).  A page with v <= kTinyV is a point mass at m: E[Y_+^k] =
+// [m]_+^k (and 0 for the density).  Branch-free: both forms are computed and
+// one is selected.
 template <int BETA>
-__device__ __forceinline__ void gauss_terms(float m, float v, float& e_b, float& e_bm1) {
+__device__ __forceinline__ void gauss_terms(float m, float v, float& e_b, float& e_b1, float& e_b2) {
     const bool point = !(v > kTinyV);
     const float vs = point ? 1.0f : v;
-    const float z = m * __builtin_amdgcn_rcpf(vs);
+    const float rv = __builtin_amdgcn_rcpf(vs);
+    const float z = m * rv;
     const float t = __builtin_amdgcn_rcpf(fmaf(kMillsK, fabsf(z), 1.0f));
     float h = kMillsC[11];
 #pragma unroll
@@ -68,48 +74,115 @@ __device__ __forceinline__ void gauss_terms(float m, float v, float& e_b, float&
     const float e1 = fmaf(m, Phi, vs * phi);
     if constexpr (BETA == 1) {
         e_b = point ? mp : e1;
-        e_bm1 = point ? (m > 0.0f ? 1.0f : 0.0f) : Phi;
+        e_b1 = point ? (m > 0.0f ? 1.0f : 0.0f) : Phi;
+        e_b2 = point ? 0.0f : phi * rv;
     } else {
         const float e2 = fmaf(fmaf(m, m, vs * vs), Phi, m * vs * phi);
         if constexpr (BETA == 2) {
             e_b = point ? mp * mp : e2;
-            e_bm1 = point ? mp : e1;
+            e_b1 = point ? mp : e1;
+            e_b2 = point ? (m > 0.0f ? 1.0f : 0.0f) : Phi;
         } else {
             const float e3 = fmaf(m * fmaf(m, m, 3.0f * vs * vs), Phi, vs * fmaf(m, m, 2.0f * vs * vs) * phi);
             e_b = point ? mp * mp * mp : e3;
-            e_bm1 = point ? mp * mp : e2;
+            e_b1 = point ? mp * mp : e2;
+            e_b2 = point ? mp : e1;
         }
     }
 }
 
-// Sums over the pages of this thread: F += n_p e_beta, D += n_p e_(beta-1).
-// Two pages per trip; only the sequence's last page can be partial.
+// Sums over this thread's pages among every S-th page p = 0, S, 2S, ...:
+// f += w_p e_beta, d1 += w_p e_(beta-1), d2 += w_p e_(beta-2), w_p = S n_p
+// (S = 1: every page with its own weight; S > 1: a subsample standing for
+// the whole sequence).  Two pages per trip; only the last page is partial.
 template <int BETA, bool STAGED>
 __device__ __forceinline__ void gauss_sums(const float2* __restrict__ lds2, const float* __restrict__ mrow,
-                                           const float* __restrict__ srow, int M, float a, float last_np,
-                                           float t, float& f, float& dsum) {
+                                           const float* __restrict__ srow, int M, int S, float a, float last_np,
+                                           float t, float& f, float& d1, float& d2) {
+    const float wS = (float)(S * kPage);
     auto page = [&](int p) {
         const float2 e = STAGED ? lds2[p] : make_float2(a * mrow[p], a * srow[p]);
-        const float np = (p == M - 1) ? last_np : (float)kPage;
-        float eb, ebm1;
-        gauss_terms<BETA>(e.x - t, e.y, eb, ebm1);
-        f = fmaf(np, eb, f);
-        dsum = fmaf(np, ebm1, dsum);
+        const float w = (p == M - 1) ? (float)S * last_np : wS;
+        float eb, eb1, eb2;
+        gauss_terms<BETA>(e.x - t, e.y, eb, eb1, eb2);
+        f = fmaf(w, eb, f);
+        d1 = fmaf(w, eb1, d1);
+        d2 = fmaf(w, eb2, d2);
     };
-    int p = threadIdx.x;
-    for (; p + kTauThreads < M; p += 2 * kTauThreads) {
+    const int step = S * kTauThreads;
+    int p = S * (int)threadIdx.x;
+    for (; p + step < M; p += 2 * step) {
         page(p);
-        page(p + kTauThreads);
+        page(p + step);
     }
     if (p < M) page(p);
 }
 
+// Root of F(tau) = 1 for one (sequence, head).  Every iteration evaluates,
+// in one pass over the pages, F = sum_p n_p E_beta, D1 = sum_p n_p E_(beta-1)
+// and D2 = sum_p n_p E_(beta-2), so that dF/dtau = -beta D1 and
+// d2F/dtau2 = beta (beta-1) D2 (beta = 1: F'' = D2, the density sum).
+// It keeps a bracket [lo, hi] with F(lo) >= 1 >= F(hi) and steps on
+// L = log F: log F is close to linear or concave over the Gaussian tails that
+// dominate F, so these steps are accurate from afar, where Newton on F itself
+// creeps (F behaves like a high power of the distance to the largest page
+// means).  beta >= 2 takes Halley steps on L (third order; D2 costs no extra
+// exp or rcp per page); beta = 1 takes Newton steps, since there the Halley
+// step on L stays bounded while F >> 1.  While F > 1 a step is capped at four
+// times the Newton step on F^(1/beta), which is convex (an L^beta norm of
+// (Y - tau)_+ over the page mixture) and so never passes the root.  A step
+// that leaves the bracket is replaced by its midpoint.
+template <int BETA>
+__device__ float gauss_tau_solve(const float2* __restrict__ lds2, const float* __restrict__ mrow,
+                                 const float* __restrict__ srow, bool staged, int M, int S, float a,
+                                 float last_np, float lo, float t, float tol, float* red, int& phase) {
+    constexpr float fb = (float)BETA;
+    float hi = INFINITY;
+    for (int it = 0; it < kTauMaxIter; ++it) {
+        float f = 0.0f, d1 = 0.0f, d2 = 0.0f;
+        if (staged) gauss_sums<BETA, true>(lds2, mrow, srow, M, S, a, last_np, t, f, d1, d2);
+        else        gauss_sums<BETA, false>(lds2, mrow, srow, M, S, a, last_np, t, f, d1, d2);
+        block_sum3<kTauWaves>(f, d1, d2, red, phase);   // block-uniform from here on
+        if (f >= 1.0f) lo = fmaxf(lo, t); else hi = fminf(hi, t);
+        if (f == 1.0f) break;
+        float step = NAN;
+        if (d1 > 0.0f && f > 0.0f) {
+            const float L = logf(f);
+            const float dL = -fb * d1 / f;                      // d log F / d tau
+            step = -L / dL;
+            if constexpr (BETA >= 2) {
+                const float d2L = fb * (fb - 1.0f) * d2 / f - dL * dL;
+                const float den = 2.0f * dL * dL - L * d2L;
+                if (den > 0.0f) step = -2.0f * L * dL / den;
+            }
+            if (f > 1.0f) {
+                const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
+                step = fminf(step, 4.0f * (1.0f - 1.0f / gr) * f / d1);
+            }
+        }
+        float nt = t + step;
+        if (!(nt >= lo && nt <= hi)) {
+            if (!(hi < INFINITY) || !(lo > -INFINITY)) break;   // no usable step, no finite bracket
+            nt = 0.5f * (lo + hi);
+            step = nt - t;
+        }
+        const bool done = fabsf(step) <= tol * fmaxf(1.0f, fabsf(t));
+        t = nt;
+        if (done) break;
+    }
+    return t;
+}
+
+// One block per (sequence, head).  The iteration first runs on every 16th
+// page (weights x16) to a loose tolerance, and the passes over all pages start
+// from that estimate: 2 to 3 full passes instead of 5 to 6 on 8192-page
+// sequences.  The full passes keep the exact lower end max_p (alpha-1) mu_p - 1.
 template <int BETA>
 __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
     const float* __restrict__ mu, const float* __restrict__ sigma, const int32_t* __restrict__ seq_lens,
     int HQ, int MP, float a, int lds_pages, float* __restrict__ tau_hat) {
     extern __shared__ float2 lds2[];               // [lds_pages] (a*mu, a*sigma) when staged
-    __shared__ float red[4 * kTauWaves];
+    __shared__ float red[6 * kTauWaves];
     int phase = 0;
     const int h = blockIdx.x, b = blockIdx.y;
     const int n = seq_len_at(seq_lens, b, MP);
@@ -131,34 +204,12 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
         if (staged) lds2[p] = make_float2(xm, a * srow[p]);
     }
     xmax = block_max<kTauWaves>(xmax, red, phase);   // barrier also publishes LDS
-
-    constexpr float fb = (float)BETA;
-    float lo = xmax - 1.0f, hi = INFINITY, t = lo;   // F(lo) >= 1 (Jensen on the top page)
-    for (int it = 0; it < kTauMaxIter; ++it) {
-        float f = 0.0f, dsum = 0.0f;
-        if (staged) gauss_sums<BETA, true>(lds2, mrow, srow, M, a, last_np, t, f, dsum);
-        else        gauss_sums<BETA, false>(lds2, mrow, srow, M, a, last_np, t, f, dsum);
-        block_sum2<kTauWaves>(f, dsum, red, phase);   // block-uniform from here on
-        if (f >= 1.0f) lo = t; else hi = t;
-        if (f == 1.0f) break;
-        float step = NAN;
-        if (dsum > 0.0f && f > 0.0f) {
-            step = logf(f) * f / (fb * dsum);
-            if (f > 1.0f) {
-                const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
-                step = fminf(step, 4.0f * (1.0f - 1.0f / gr) * f / dsum);
-            }
-        }
-        float nt = t + step;
-        if (!(nt >= lo && nt <= hi)) {
-            if (!(hi < INFINITY)) break;          // no usable step and no upper end yet
-            nt = 0.5f * (lo + hi);
-            step = nt - t;
-        }
-        const bool done = fabsf(step) <= kTauTol * fmaxf(1.0f, fabsf(t));
-        t = nt;
-        if (done) break;
-    }
+    const float lo = xmax - 1.0f;                    // F(lo) >= 1 (Jensen on the top page)
+    float t = lo;
+    if (M >= kTauSubMin)                             // no lower end known for the subsample
+        t = gauss_tau_solve<BETA>(lds2, mrow, srow, staged, M, kTauSub, a, last_np, -INFINITY, lo,
+                                  kTauSubTol, red, phase);
+    t = gauss_tau_solve<BETA>(lds2, mrow, srow, staged, M, 1, a, last_np, lo, t, kTauTol, red, phase);
     if (threadIdx.x == 0) *out = t;
 }
 

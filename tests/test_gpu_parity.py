@@ -31,6 +31,13 @@ def workload(name):
         return W.make_workload(W.CONFIGS[3].scaled(batch=2), "cuda", seq_lens=[8197, 3001])
     if name == "with-empty":
         return W.make_workload(W.CONFIGS[2].scaled(batch=3), "cuda", seq_lens=[700, 0, 1601])
+    if name == "flat":
+        # nearly equal keys: the entmax support covers most selected tokens
+        # (thousands per head), past what the decode keeps in LDS at once
+        wl = W.make_workload(W.CONFIGS[2].scaled(batch=2), "cuda", seq_lens=[3000, 2400])
+        g = torch.Generator(device="cuda").manual_seed(11)
+        wl.k_cache.copy_((torch.randn(wl.k_cache.shape, generator=g, device="cuda") * 0.02).to(wl.k_cache.dtype))
+        return wl
     raise KeyError(name)
 
 
@@ -248,14 +255,16 @@ def test_full_cache_decode(name, alpha):
             assert abs(int(sup[b, h]) - int(ref["support"][h])) <= slack
 
 
-@pytest.mark.parametrize("name,alpha", [("tiny", 1.5), ("tiny", 2.0), ("tiny", 1.0), ("llama-ragged", 1.5),
-                                        ("llama-ragged", 1.0), ("llama-ragged", 2.0), ("gauss-ragged", 1.5)])
+@pytest.mark.parametrize("name,alpha", [("tiny", 1.5), ("tiny", 2.0), ("tiny", 1.0), ("tiny", 4.0 / 3.0),
+                                        ("tiny", 3.0), ("llama-ragged", 1.5), ("llama-ragged", 1.0),
+                                        ("llama-ragged", 2.0), ("gauss-ragged", 1.5), ("flat", 1.5), ("flat", 2.0),
+                                        ("flat", 4.0 / 3.0)])
 def test_sparse_decode_on_oracle_selection(name, alpha):
     """Decode over a given selection (the oracle's top-k), with the dropped
     mass measured against the full-cache threshold."""
     wl = workload(name)
     c = wl.cfg
-    budget = c.budget_pages if name != "gauss-ragged" else 64
+    budget = {"gauss-ragged": 64, "flat": 256}.get(name, c.budget_pages)
     sels, fulls = [], []
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
