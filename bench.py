@@ -70,6 +70,34 @@ def score_kernel_bytes(wl, selector, stat_bytes):
     return rd + wr
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gauss_score_kernel_traffic_batched-128k-clustered.md")
+
+
+def measured_traffic(workload, stat_dtype):
+    """HBM bytes per launch of the Gaussian score kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy of known
+    size), or None when the workload differs or the kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+    if workload != "batched-128k-clustered" or stat_dtype != "f32" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if ": " in line and not line.startswith(("#", "|")):
+            k, v = line.split(": ", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in kv["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, selector, alpha, budget, z, nseq, stat_round=None):
     """The fp64 oracle on a bounded sample of sequences, same stages as the
     timed GPU step (statistics precomputed, untimed)."""
@@ -121,9 +149,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--stat-dtype", default="f32", choices=["f32", "bf16"])
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this many bytes "
+                         "(a kernel of known traffic for scaling hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -180,6 +211,15 @@ def main():
     log(f"{args.steps} timed steps: {wall * 1e3 / args.steps:.3f} ms/step wall, "
         f"median event {statistics.median(step_ms):.3f} ms, score kernel {statistics.mean(score_ms) * 1e3:.1f} us")
 
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {args.copy_bytes} bytes done")
+
     stat_bytes = 4 if args.stat_dtype == "f32" else 2
     e_kv = 2 if cfg.kv_dtype == "bf16" else 4
     meta, k_sel, v_sup, small = step_bytes(wl, selector, stat_bytes, dec.buf.sel_count, dec.buf.support, e_kv)
@@ -212,7 +252,9 @@ def main():
         "median_event_ms_per_step": round(statistics.median(step_ms), 4),
         "roofline": {"kernel": "gauss_score_kernel" if selector == "gauss" else "box_score_kernel",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(cfg.name, args.stat_dtype) if selector == "gauss" else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": sk_bytes, "avg_launch_us": round(sk_us, 2)},
     }
 

@@ -72,3 +72,52 @@ def to_np(t):
 
 def sync():
     torch.cuda.synchronize()
+
+
+def seq_pages_f64(cache, wl, b, pages):
+    """float64 [len(pages)][G][P][d] copy of the given logical pages of
+    sequence b from a paged cache (only those pages leave the GPU)."""
+    phys = wl.page_table[b, torch.as_tensor(np.asarray(pages, dtype=np.int64), device=wl.page_table.device)].long()
+    return cache[phys].double().cpu().numpy()
+
+
+def seq_stats_chunked(wl, b, chunk_pages=4096):
+    """Oracle page statistics of sequence b over all its pages, computed in
+    chunks of whole pages so that only one chunk of K is on the host at a
+    time.  Returns (kmin, kmax, mean, var) [M][G][d] and n."""
+    P = wl.cfg.page_size
+    n = wl.seq_lens_host[b]
+    M = (n + P - 1) // P
+    outs = []
+    for c0 in range(0, M, chunk_pages):
+        c1 = min(M, c0 + chunk_pages)
+        tiles = seq_pages_f64(wl.k_cache, wl, b, np.arange(c0, c1))        # [m][G][P][d]
+        m = c1 - c0
+        K = tiles.transpose(0, 2, 1, 3).reshape(m * P, tiles.shape[1], tiles.shape[3])
+        valid = min(n, c1 * P) - c0 * P
+        outs.append(oracle.paged.page_stats(K[:valid], P))
+    return tuple(np.concatenate([o[i] for o in outs]) for i in range(4)), n
+
+
+def seq_tokens_f64(cache, wl, b, tokens):
+    """float64 [len(tokens)][G][d] of the given token positions of sequence b."""
+    P = wl.cfg.page_size
+    tokens = np.asarray(tokens, dtype=np.int64)
+    pages = np.unique(tokens // P)
+    tiles = seq_pages_f64(cache, wl, b, pages)                             # [m][G][P][d]
+    where = {int(p): i for i, p in enumerate(pages)}
+    idx = np.array([where[int(t // P)] for t in tokens])
+    return tiles[idx, :, tokens % P, :]
+
+
+def seq_scores_chunked(wl, b, q, chunk_tokens=1 << 17):
+    """Oracle token scores s_{h,j} [H][n] of sequence b over all its tokens,
+    in chunks of whole pages."""
+    P = wl.cfg.page_size
+    n = wl.seq_lens_host[b]
+    out = []
+    for t0 in range(0, n, chunk_tokens):
+        t1 = min(n, t0 + chunk_tokens)
+        K = seq_tokens_f64(wl.k_cache, wl, b, np.arange(t0, t1))
+        out.append(oracle.paged.token_scores(q, K))
+    return np.concatenate(out, axis=1)

@@ -1,0 +1,179 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch
+configuration bench.py times (ekv.Decoder: score -> select -> decode), on
+sampled sequences that the fp64 oracle recomputes from the same device
+inputs (copied to the host in chunks).  Stages and rules: "EntmaxKV:
+Support-Aware Decoding for Entmax Attention" section 4.1 (decode on the
+selected pages), 4.2 / Appendix B.1 (box scores), 4.3 / Appendix C.2 Eq. (18)
+(Gaussian threshold and page rule), 3.1 (dropped mass).  Tolerances are those
+of tests/gpu_helpers.py."""
+
+import functools
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_long_context_ekv_amd import ekv
+from sparse_long_context_ekv_amd import workloads as W
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+P = 16
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_decode_on_selection(wl, dec, b, q, alpha, sels):
+    """Output, tau and support of sequence b against the oracle's decode over
+    the GPU's own selection (one page set per KV group)."""
+    c = wl.cfg
+    G, r = c.num_kv_groups, c.num_q_heads // c.num_kv_groups
+    for g in range(G):
+        toks = oracle.decode.tokens_of_pages(sels[g], wl.seq_lens_host[b], P)
+        K = H.seq_tokens_f64(wl.k_cache, wl, b, toks)[:, g:g + 1, :]
+        V = H.seq_tokens_f64(wl.v_cache, wl, b, toks)[:, g:g + 1, :]
+        ref = oracle.decode.decode(q[g * r:(g + 1) * r], K, V, None, alpha)
+        got = H.to_np(dec.buf.out[b, g * r:(g + 1) * r])
+        assert np.abs(got - ref["out"]).max() <= H.OUT_ATOL, (b, g, np.abs(got - ref["out"]).max())
+        for j in range(r):
+            h = g * r + j
+            assert H.tau_close(float(dec.buf.tau[b, h]), ref["tau"][j]), (b, h, float(dec.buf.tau[b, h]), ref["tau"][j])
+            if alpha > 1.0:
+                x = (alpha - 1.0) * ref["s"][j]
+                slack = int(np.count_nonzero(np.abs(x - ref["tau"][j]) < 1e-5 * max(1.0, abs(ref["tau"][j]))))
+                assert abs(int(dec.buf.support[b, h]) - int(ref["support"][j])) <= slack
+
+
+def _gpu_selection(dec, b, G):
+    return [dec.buf.sel_pages[b, g, :int(dec.buf.sel_count[b, g])].cpu().numpy() for g in range(G)]
+
+
+def test_batched_128k_gaussian_fullsize():
+    """The headline workload: B=16, 32/8 heads, d=128, 131072 tokens each,
+    Gaussian selector capped at 256 pages, fp32 statistics."""
+    cfg = W.CONFIGS[3]
+    print(f"[case] {cfg.name}", flush=True)
+    wl = W.make_workload(cfg, "cuda")
+    dec = ekv.Decoder(wl, "gauss", 1.5, cfg.budget_pages, z=cfg.z)
+    dec.build_stats()
+    dec.step()
+    full = ekv.FullDecoder(wl, 1.5)
+    full.run()
+    delta = torch.empty_like(dec.buf.tau)
+    dec.decode(tau_ref=full.tau, delta=delta)
+    H.sync()
+    G, HQ = cfg.num_kv_groups, cfg.num_q_heads
+    r = HQ // G
+    for b in (0, cfg.batch - 1):
+        print(f"[case] {cfg.name} b={b}", flush=True)
+        q = H.to_np(wl.q[b])
+        (kmin, kmax, mean, var), n = H.seq_stats_chunked(wl, b)
+        M = mean.shape[0]
+        n_p = oracle.paged.page_valid_counts(n, P)
+        mu, sg = oracle.paged.gauss_moments(q, mean, var)
+        np.testing.assert_allclose(H.to_np(dec.buf.mu[b, :, :M]), mu, rtol=1e-5, atol=1e-5 * np.abs(mu).max())
+        np.testing.assert_allclose(H.to_np(dec.buf.sigma[b, :, :M]), sg, rtol=1e-5, atol=1e-5 * np.abs(sg).max())
+        th = np.array([oracle.select.gauss_tau_hat(mu[h], sg[h], n_p, 1.5) for h in range(HQ)])
+        got_th = H.to_np(dec.buf.tau_hat[b])
+        for h in range(HQ):
+            assert H.tau_close(got_th[h], th[h]), (b, h, got_th[h], th[h])
+        sels = _gpu_selection(dec, b, G)
+        for g in range(G):
+            hs = slice(g * r, (g + 1) * r)
+            t = oracle.select.gauss_margins(mu[hs], sg[hs], th[hs], 1.5)
+            want = oracle.select.gauss_select(mu[hs], sg[hs], th[hs], 1.5, cfg.z, cfg.budget_pages)
+            assert len(sels[g]) == len(want)
+            H.compare_selection(sels[g], want, t, len(want))
+        _check_decode_on_selection(wl, dec, b, q, 1.5, sels)
+        # dropped mass against the oracle's full-cache distribution
+        s = H.seq_scores_chunked(wl, b, q)
+        for h in range(HQ):
+            p, tau_full, _ = oracle.entmax.entmax(s[h], 1.5)
+            assert H.tau_close(float(full.tau[b, h]), tau_full)
+            toks = oracle.decode.tokens_of_pages(sels[h // r], n, P)
+            d_or = 1.0 - p[toks].sum()
+            assert abs(float(delta[b, h]) - d_or) <= H.DELTA_ATOL, (b, h, float(delta[b, h]), d_or)
+        del s
+    del dec, full, wl
+
+
+def test_extreme_1m_topk_and_full_cache():
+    """B=1, 1,048,576 tokens: box scores of all 65536 pages, exact top-256
+    selection, sparse decode, and the full-cache decode over every token."""
+    cfg = W.CONFIGS[4]
+    print(f"[case] {cfg.name}", flush=True)
+    wl = W.make_workload(cfg, "cuda")
+    dec = ekv.Decoder(wl, "topk", 1.5, cfg.budget_pages)
+    dec.build_stats()
+    dec.step()
+    full = ekv.FullDecoder(wl, 1.5)
+    full.run()
+    H.sync()
+    G, HQ = cfg.num_kv_groups, cfg.num_q_heads
+    b = 0
+    q = H.to_np(wl.q[b])
+    (kmin, kmax, _, _), n = H.seq_stats_chunked(wl, b)
+    M = kmin.shape[0]
+    _, U = oracle.paged.box_scores(q, kmin, kmax)
+    got = H.to_np(dec.buf.score[b, :, :M])
+    np.testing.assert_allclose(got, U, rtol=1e-5, atol=1e-5 * np.abs(U).max())
+    sels = _gpu_selection(dec, b, G)
+    for g in range(G):
+        want = oracle.select.topk_pages(U[g], cfg.budget_pages)
+        H.compare_selection(sels[g], want, U[g], len(want))
+    _check_decode_on_selection(wl, dec, b, q, 1.5, sels)
+    # full cache: every token
+    s = H.seq_scores_chunked(wl, b, q)
+    r = HQ // G
+    for h in range(HQ):
+        p, tau_full, k = oracle.entmax.entmax(s[h], 1.5)
+        assert H.tau_close(float(full.tau[b, h]), tau_full), (h, float(full.tau[b, h]), tau_full)
+        nz = np.flatnonzero(p)
+        V = H.seq_tokens_f64(wl.v_cache, wl, b, nz)[:, h // r, :]
+        o = p[nz] @ V
+        assert np.abs(H.to_np(full.out[b, h]) - o).max() <= H.OUT_ATOL
+        assert abs(int(full.support[b, h]) - k) <= int(np.count_nonzero(
+            np.abs(0.5 * s[h] - tau_full) < 1e-5 * max(1.0, abs(tau_full))))
+    del s, dec, full, wl
+
+
+@functools.lru_cache(maxsize=1)
+def _ragged_workload():
+    return W.make_workload(W.CONFIGS[5], "cuda")
+
+
+@pytest.mark.parametrize("alpha", [1.0, 1.5, 2.0])
+def test_ragged_alpha_sweep_fullsize(alpha):
+    """B=64, lengths log-uniform in [4096, 262144], top-k 128 pages per
+    (sequence, group), alpha in {1 (softmax top-k), 1.5, 2 (sparsemax)}."""
+    cfg = W.CONFIGS[5]
+    print(f"[case] {cfg.name} alpha={alpha}", flush=True)
+    wl = _ragged_workload()
+    dec = ekv.Decoder(wl, "topk", alpha, cfg.budget_pages)
+    dec.build_stats()
+    dec.step()
+    H.sync()
+    G = cfg.num_kv_groups
+    lens = wl.seq_lens_host
+    picks = sorted({0, int(np.argmin(lens)), int(np.argmax(lens)), cfg.batch - 1})
+    for b in picks:
+        print(f"[case] {cfg.name} alpha={alpha} b={b} n={lens[b]}", flush=True)
+        q = H.to_np(wl.q[b])
+        (kmin, kmax, _, _), n = H.seq_stats_chunked(wl, b)
+        M = kmin.shape[0]
+        _, U = oracle.paged.box_scores(q, kmin, kmax)
+        np.testing.assert_allclose(H.to_np(dec.buf.score[b, :, :M]), U, rtol=1e-5, atol=1e-5 * np.abs(U).max())
+        sels = _gpu_selection(dec, b, G)
+        for g in range(G):
+            want = oracle.select.topk_pages(U[g], cfg.budget_pages)
+            H.compare_selection(sels[g], want, U[g], len(want))
+        _check_decode_on_selection(wl, dec, b, q, alpha, sels)
+    del dec
