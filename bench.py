@@ -152,6 +152,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many bytes "
                          "(a kernel of known traffic for scaling hardware byte counters)")
@@ -259,17 +260,21 @@ def main():
     }
 
     # Quality of the selection: dropped mass against the full-cache threshold.
-    if not args.no_full:
-        full = ekv.FullDecoder(wl, alpha)
-        full.run()
+    def time_full(runner, reps=5):
+        runner()
         torch.cuda.synchronize()
-        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b2 in fe:
             a.record(stream)
-            full.run()
+            runner()
             b2.record(stream)
         torch.cuda.synchronize()
-        full_ms = statistics.median([a.elapsed_time(b2) for a, b2 in fe])
+        return statistics.median([a.elapsed_time(b2) for a, b2 in fe])
+
+    if not args.no_full:
+        # Full-cache baselines on the same inputs: entmax (same alpha) and softmax.
+        full = ekv.FullDecoder(wl, alpha)
+        full_ms = time_full(full.run)
         delta = torch.empty_like(dec.buf.tau)
         dec.decode(tau_ref=full.tau, delta=delta)
         torch.cuda.synchronize()
@@ -280,6 +285,44 @@ def main():
                                 "speedup_sparse_over_full": round(full_ms / ms_per_step, 3)}
         result["quality"] = {"coverage": round(cov, 5), "delta_mean": float(delta.mean()),
                              "delta_max": float(delta.max()), "R_mean": float(rel.mean()), "R_max": float(rel.max())}
+        del full
+        soft = ekv.FullDecoder(wl, 1.0)
+        soft_ms = time_full(soft.run)
+        result["full_cache_softmax"] = {"ms_per_step": round(soft_ms, 4),
+                                        "speedup_sparse_over_full": round(soft_ms / ms_per_step, 3)}
+        del soft
+        torch.cuda.synchronize()
+        log(f"full-cache entmax {full_ms:.3f} ms, softmax {soft_ms:.3f} ms per step")
+
+    if not args.no_variants and selector == "gauss" and args.stat_dtype == "f32":
+        # Same step with the page mean/variance stored in bf16 (half the
+        # statistics bytes); reported beside the fp32 headline, not as it.
+        dec16 = ekv.Decoder(wl, selector, alpha, budget, z=z, stat_dtype="bf16")
+        dec16.build_stats()
+        for _ in range(max(args.warmup // 2, 3)):
+            dec16.step()
+        torch.cuda.synchronize()
+        ev16 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                 torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a, b2, c2 in ev16:
+            a.record(stream)
+            dec16.score()
+            b2.record(stream)
+            dec16.select()
+            dec16.decode()
+            c2.record(stream)
+        torch.cuda.synchronize()
+        wall16 = time.perf_counter() - t0
+        sk16 = statistics.mean([a.elapsed_time(b2) for a, b2, _ in ev16]) * 1e3
+        b16 = score_kernel_bytes(wl, selector, 2)
+        result["variants"] = {"bf16_page_mean_var": {
+            "value": round(args.steps / wall16, 3), "unit": "steps/s",
+            "ms_per_step": round(wall16 * 1e3 / args.steps, 4),
+            "score_kernel_us": round(sk16, 2), "score_kernel_gbps": round(b16 / (sk16 * 1e-6) / 1e9, 1),
+            "note": "page mean/variance stored as bf16 (fp32 accumulation); min/max unaffected"}}
+        del dec16
+        torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         rnd = None
