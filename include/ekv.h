@@ -73,8 +73,9 @@ typedef enum {
 typedef enum { EKV_F32 = 0, EKV_BF16 = 1 } ekv_dtype;
 
 typedef enum {
-    EKV_SEL_TOPK = 0,   /* [EKV] section 4.3 "Top-k page selection"            */
-    EKV_SEL_GAUSS = 1   /* [EKV] section 4.3 "Gaussian-aware entmax selection"  */
+    EKV_SEL_TOPK = 0,     /* [EKV] section 4.3 "Top-k page selection"            */
+    EKV_SEL_GAUSS = 1,    /* [EKV] section 4.3 "Gaussian-aware entmax selection"  */
+    EKV_SEL_SUPERSET = 2  /* [EKV] Appendix B.2 support-superset selection        */
 } ekv_selector;
 
 /* Problem shape.  Supported: D in {64, 128}; P == 16; r in {1, 2, 4, 8};
@@ -127,7 +128,7 @@ ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void*
                            float* score, float* mu, float* sigma, void* stream);
 
 /* Candidate page selection, one page set per (sequence, KV group)
- * ([EKV] section 4.3).
+ * ([EKV] section 4.3; Appendix B.2).
  * EKV_SEL_TOPK: the min(budget_pages, M_b) pages with the largest score;
  *   ties go to the lower logical page index.  `alpha`, `z`, mu, sigma unused.
  * EKV_SEL_GAUSS: per head, tau_hat solves the distributional threshold
@@ -140,9 +141,22 @@ ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void*
  *   (the page rule of Eq. (21) is not legible on the page; this is the reading
  *   this library takes); candidates are ranked by that margin (ties to the
  *   lower index) and at most budget_pages are kept; at least one page is kept.
+ * EKV_SEL_SUPERSET (alpha > 1): `score` holds the box scores of
+ *   EKV_SEL_TOPK scoring (upper bounds on every token score of a page) and
+ *   tau_hat is an INPUT: per head, a threshold (x units) no larger than that
+ *   head's full-cache entmax threshold -- e.g. the tau that
+ *   ekv_entmax_decode returns for any subset of the tokens, which can only be
+ *   smaller.  Page p of group g is a candidate when
+ *       score_{g,p} >= min_{h in g} tau_hat_h / (alpha-1) - 1e-5 |.|
+ *   (the relative slack absorbs fp32 rounding, so it only ever adds pages);
+ *   candidates are ranked by score (ties to the lower index), at most
+ *   budget_pages kept, at least one.  Whenever no candidate is cut by the
+ *   budget, the selection contains every token of the entmax support of every
+ *   head of the group, and decoding on it is exact (dropped mass 0).
  * Outputs: sel_pages [B][G][budget_pages] int32 logical indices in ascending
  *   order, unused tail = -1; sel_count [B][G] int32; tau_hat [B][HQ] fp32
- *   (GAUSS only; may be NULL).  Needs a workspace (see conventions).       */
+ *   (GAUSS: output, may be NULL; SUPERSET: required input).  Needs a
+ *   workspace (see conventions).                                            */
 ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* seq_lens,
                       float alpha, int32_t budget_pages, float z,
                       const float* score, const float* mu, const float* sigma,

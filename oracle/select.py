@@ -143,3 +143,23 @@ def gauss_select(mu: np.ndarray, sigma: np.ndarray, tau_hat: np.ndarray, alpha: 
     count = int(np.count_nonzero(t >= -z))
     take = max(1, min(count, cap))
     return np.sort(order[:take])
+
+
+def superset_pages(U: np.ndarray, tau_lo: np.ndarray, alpha: float, cap: int) -> np.ndarray:
+    """Support-superset selection for one KV group ([EKV] Appendix B.2): with
+    U_p an upper bound on every token score of page p (the box score) and
+    tau_lo_h no larger than head h's threshold, any token j with
+    (alpha-1) s_j > tau_h lies in a page with (alpha-1) U_p > tau_lo_h.  One
+    page set serves the group (reading R5), so the group's threshold is the
+    smallest of its heads': select every page with
+    U_p > min_h tau_lo_h / (alpha-1), ranked by U (ties to the lower index),
+    at most cap pages, at least one; ascending order.
+
+    U: [M] pooled box scores; tau_lo: [r] per-head thresholds in x units."""
+    U = np.asarray(U, dtype=np.float64)
+    theta = float(np.min(np.asarray(tau_lo, dtype=np.float64))) / (alpha - 1.0)
+    M = U.size
+    order = np.lexsort((np.arange(M), -U))
+    count = int(np.count_nonzero(U > theta))
+    take = max(1, min(count, cap))
+    return np.sort(order[:take])

@@ -128,15 +128,18 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
     if (st != EKV_OK) return st;
     if (!workspace_bytes) return fail(EKV_ERR_INVALID_ARG, "workspace_bytes is NULL");
     if (budget_pages < 1) return fail(EKV_ERR_INVALID_ARG, "budget_pages=%d < 1", budget_pages);
-    if (selector != EKV_SEL_TOPK && selector != EKV_SEL_GAUSS)
+    if (selector != EKV_SEL_TOPK && selector != EKV_SEL_GAUSS && selector != EKV_SEL_SUPERSET)
         return fail(EKV_ERR_INVALID_ARG, "unknown selector %d", selector);
     const bool gauss = selector == EKV_SEL_GAUSS;
+    const bool superset = selector == EKV_SEL_SUPERSET;
     if (gauss) {
         if (!(alpha > 1.0f)) return fail(EKV_ERR_INVALID_ARG, "Gaussian selection needs alpha > 1 (got %g)", alpha);
         if (!gauss_alpha_ok(alpha))
             return fail(EKV_ERR_UNSUPPORTED, "Gaussian selection built for alpha in {2, 3/2, 4/3} (got %g)", alpha);
         if (!(z == z)) return fail(EKV_ERR_INVALID_ARG, "z is NaN");
     }
+    if (superset && !(alpha > 1.0f)) return fail(EKV_ERR_INVALID_ARG, "superset selection needs alpha > 1 (got %g)", alpha);
+    if (superset && !(alpha < 1e6f)) return fail(EKV_ERR_INVALID_ARG, "alpha out of range (got %g)", alpha);
     const size_t keys_bytes = align256((size_t)d.B * d.G * d.MP * sizeof(uint32_t));
     const size_t tau_bytes = gauss ? align256((size_t)d.B * d.HQ * sizeof(float)) : 0;
     const size_t need = keys_bytes + tau_bytes;
@@ -149,6 +152,7 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
     if (((uintptr_t)workspace & 255) != 0) return fail(EKV_ERR_INVALID_ARG, "workspace not 256-byte aligned");
     if (!seq_lens || !sel_pages || !sel_count) return fail(EKV_ERR_INVALID_ARG, "seq_lens, sel_pages and sel_count are required");
     if (gauss ? (!mu || !sigma) : !score) return fail(EKV_ERR_INVALID_ARG, "missing page scores for the selector");
+    if (superset && !tau_hat) return fail(EKV_ERR_INVALID_ARG, "superset selection needs tau_hat (per-head lower bounds)");
     uint32_t* keys = (uint32_t*)workspace;
     float* th = tau_hat ? tau_hat : (float*)((char*)workspace + keys_bytes);
     hipStream_t s = (hipStream_t)stream;
@@ -156,7 +160,7 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
         hipError_t e = ekv::launch_gauss_tau(d, mu, sigma, seq_lens, alpha, th, s);
         if (e != hipSuccess) return hip_status(e, "ekv_select (threshold estimate)");
     }
-    return hip_status(ekv::launch_select(d, gauss ? 1 : 0, seq_lens, alpha, budget_pages, z, score, mu, sigma,
+    return hip_status(ekv::launch_select(d, selector, seq_lens, alpha, budget_pages, z, score, mu, sigma,
                                          th, keys, sel_pages, sel_count, s),
                       "ekv_select");
 }

@@ -28,10 +28,11 @@ hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_
                               const int32_t* seq_lens, const void* kmean, const void* kvar,
                               float* mu, float* sigma, hipStream_t s);
 
-// Selection.  `keys` is workspace [B][G][MP] uint32.
+// Selection.  mode: 0 top-k, 1 Gaussian, 2 support superset (ekv_selector).
+// `keys` is workspace [B][G][MP] uint32.
 hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
                             const int32_t* seq_lens, float alpha, float* tau_hat, hipStream_t s);
-hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, float alpha,
+hipError_t launch_select(const Dims& d, int mode, const int32_t* seq_lens, float alpha,
                          int budget, float z, const float* score, const float* mu,
                          const float* sigma, const float* tau_hat, uint32_t* keys,
                          int32_t* sel_pages, int32_t* sel_count, hipStream_t s);

@@ -214,6 +214,31 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
 }
 
 // --------------------------------------------------------------- select ----
+enum { kSelTopk = 0, kSelGauss = 1, kSelSuperset = 2 };
+
+// Cutoff key of a (sequence, group): candidates are keys >= cut.
+//  top-k: every page;  Gaussian: margin >= -z;
+//  superset: box score >= min over the group's heads of tau_lo / (alpha-1),
+//  lowered by 1e-5 relative so that fp32 rounding of the scores and of the
+//  lower bound can only add pages, never drop one the exact rule keeps.
+template <int MODE, int R>
+__device__ __forceinline__ uint32_t select_cut(const float* __restrict__ tau_hat, size_t head0, float inv_a,
+                                               float zcut) {
+    if constexpr (MODE == kSelGauss) {
+        return ord_key(-zcut);
+    } else if constexpr (MODE == kSelSuperset) {
+        float th = INFINITY;
+#pragma unroll
+        for (int j = 0; j < R; ++j) th = fminf(th, tau_hat[head0 + j]);
+        th *= inv_a;
+        th -= 1e-5f * fmaxf(1.0f, fabsf(th));
+        return th > -INFINITY ? ord_key(th) : 0u;    // -inf or NaN: every page
+    } else {
+        return 0u;
+    }
+}
+
+
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
@@ -238,7 +263,7 @@ __device__ __forceinline__ int block_excl_scan(bool flag, int* wsum, int* total)
     return off + below;
 }
 
-template <int GAUSS, int R>
+template <int MODE, int R>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
     const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
@@ -256,16 +281,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* out = sel_pages + ((size_t)b * G + g) * budget;
 
     // Pass A: keys, and the count of candidates at or above the cutoff.
-    const uint32_t cut = GAUSS ? ord_key(-zcut) : 0u;
+    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
     float theta[R];
-    if constexpr (GAUSS) {
+    if constexpr (MODE == kSelGauss) {
 #pragma unroll
         for (int j = 0; j < R; ++j) theta[j] = tau_hat[(size_t)b * HQ + g * R + j] * inv_a;
     }
     float cnt = 0.0f;
     for (int p = threadIdx.x; p < M; p += kSelThreads) {
         float f;
-        if constexpr (GAUSS) {
+        if constexpr (MODE == kSelGauss) {
             f = -INFINITY;
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -388,7 +413,7 @@ __device__ __forceinline__ void load_span(const float* __restrict__ row, int p0,
 // owns the KPT consecutive pages [t*KPT, (t+1)*KPT), so one block-wide scan of
 // per-thread counts places every kept page in ascending order.  Needs
 // M <= KPT * kSelThreads.
-template <int GAUSS, int R, int KPT>
+template <int MODE, int R, int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
     const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
@@ -404,7 +429,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
 
     // Keys: pooled box score, or pooled Gaussian margin.
     uint32_t key[KPT];
-    if constexpr (GAUSS) {
+    if constexpr (MODE == kSelGauss) {
         constexpr int C = KPT < 8 ? KPT : 8;      // pages per sub-chunk (bounds registers)
 #pragma unroll
         for (int c0 = 0; c0 < KPT; c0 += C) {
@@ -436,7 +461,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     }
 
     // Candidates (key >= cut): their count and key range.
-    const uint32_t cut = GAUSS ? ord_key(-zcut) : 0u;
+    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
     int cnt = 0;
     uint32_t cmin = 0xffffffffu, cmax = 0u;
 #pragma unroll
@@ -585,7 +610,7 @@ hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
     }
 }
 
-hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, float alpha,
+hipError_t launch_select(const Dims& d, int mode, const int32_t* seq_lens, float alpha,
                          int budget, float z, const float* score, const float* mu,
                          const float* sigma, const float* tau_hat, uint32_t* keys,
                          int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
@@ -595,36 +620,38 @@ hipError_t launch_select(const Dims& d, int gauss, const int32_t* seq_lens, floa
     int kpt = 0;
     for (int k = 4; k <= 64; k *= 2)
         if ((long)k * kSelThreads >= d.MP) { kpt = k; break; }
-#define EKV_SELR(RR, GG, KK)                                                                          \
-    select_reg_kernel<GG, RR, KK><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score, \
+#define EKV_SELR(MM, RR, KK)                                                                              \
+    select_reg_kernel<MM, RR, KK><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score,  \
                                                                      mu, sigma, tau_hat, inv_a, z,        \
                                                                      sel_pages, sel_count);               \
     return hipGetLastError();
-#define EKV_SELK(RR, GG)                                     \
+#define EKV_SELK(MM, RR)                                     \
     switch (kpt) {                                           \
-        case 4: { EKV_SELR(RR, GG, 4) }                      \
-        case 8: { EKV_SELR(RR, GG, 8) }                      \
-        case 16: { EKV_SELR(RR, GG, 16) }                    \
-        case 32: { EKV_SELR(RR, GG, 32) }                    \
-        case 64: { EKV_SELR(RR, GG, 64) }                    \
+        case 4: { EKV_SELR(MM, RR, 4) }                      \
+        case 8: { EKV_SELR(MM, RR, 8) }                      \
+        case 16: { EKV_SELR(MM, RR, 16) }                    \
+        case 32: { EKV_SELR(MM, RR, 32) }                    \
+        case 64: { EKV_SELR(MM, RR, 64) }                    \
         default: break;                                      \
     }
-#define EKV_SEL(RR, GG)                                                                              \
-    select_kernel<GG, RR><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score, mu, \
+#define EKV_SEL(MM, RR)                                                                              \
+    select_kernel<MM, RR><<<grid, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score, mu, \
                                                              sigma, tau_hat, inv_a, z, keys,          \
                                                              sel_pages, sel_count);                   \
     return hipGetLastError();
-    if (gauss) {
-        switch (d.R) {
-            case 1: { EKV_SELK(1, 1) EKV_SEL(1, 1) }
-            case 2: { EKV_SELK(2, 1) EKV_SEL(2, 1) }
-            case 4: { EKV_SELK(4, 1) EKV_SEL(4, 1) }
-            case 8: { EKV_SELK(8, 1) EKV_SEL(8, 1) }
-            default: return hipErrorInvalidValue;
-        }
+#define EKV_SELM(MM)                                         \
+    switch (d.R) {                                           \
+        case 1: { EKV_SELK(MM, 1) EKV_SEL(MM, 1) }           \
+        case 2: { EKV_SELK(MM, 2) EKV_SEL(MM, 2) }           \
+        case 4: { EKV_SELK(MM, 4) EKV_SEL(MM, 4) }           \
+        case 8: { EKV_SELK(MM, 8) EKV_SEL(MM, 8) }           \
+        default: return hipErrorInvalidValue;                \
     }
-    EKV_SELK(1, 0)
-    EKV_SEL(1, 0)
+    if (mode == kSelGauss) { EKV_SELM(kSelGauss) }
+    if (mode == kSelSuperset) { EKV_SELM(kSelSuperset) }
+    EKV_SELK(kSelTopk, 1)
+    EKV_SEL(kSelTopk, 1)
+#undef EKV_SELM
 #undef EKV_SEL
 #undef EKV_SELK
 #undef EKV_SELR

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libekv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-SEL_TOPK, SEL_GAUSS = 0, 1
+SEL_TOPK, SEL_GAUSS, SEL_SUPERSET = 0, 1, 2
 _STATUS = {0: "EKV_OK", 1: "EKV_ERR_INVALID_ARG", 2: "EKV_ERR_UNSUPPORTED", 3: "EKV_ERR_WORKSPACE", 4: "EKV_ERR_HIP"}
 SYMBOLS = ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
            "ekv_last_error", "ekv_abi_version")
@@ -169,13 +169,21 @@ class StepBuffers:
 
 class Decoder:
     """Buffers and calls for one decode step of a workload:
-    ekv_score_pages -> ekv_select -> ekv_entmax_decode, all on one stream."""
+    ekv_score_pages -> ekv_select -> ekv_entmax_decode, all on one stream.
+
+    selector "topk" | "gauss" | "superset".  "superset" (alpha > 1) scores
+    pages by box bounds, decodes over the top `first_pages` pages to get a
+    threshold no larger than the full-cache one (the threshold of any token
+    subset is), then selects every page whose box bound clears it
+    (EKV_SEL_SUPERSET) and decodes on that set; with budget_pages at least the
+    number of qualifying pages the result is exact."""
 
     def __init__(self, wl, selector: str, alpha: float, budget_pages: int, z: float = 3.0,
-                 stat_dtype: str = "f32"):
+                 stat_dtype: str = "f32", first_pages: int = 8):
         c = wl.cfg
         dev = wl.k_cache.device
         self.wl = wl
+        self.superset = selector == "superset"
         self.selector = SEL_GAUSS if selector == "gauss" else SEL_TOPK
         self.alpha = float(alpha)
         self.budget = int(budget_pages)
@@ -208,6 +216,18 @@ class Decoder:
             ws_decode=torch.empty(decode_workspace_bytes(self.shape, True, self.budget, self.alpha),
                                   dtype=torch.uint8, device=dev),
         )
+        self.first = None
+        if self.superset:
+            k0 = int(first_pages)
+            self.first = {
+                "pages": k0,
+                "sel": torch.empty(B, G, k0, dtype=torch.int32, device=dev),
+                "cnt": torch.empty(B, G, dtype=torch.int32, device=dev),
+                "out": torch.empty(B, H, D, **f32),
+                "tau": torch.empty(B, H, **f32),
+                "ws": torch.empty(decode_workspace_bytes(self.shape, True, k0, self.alpha), dtype=torch.uint8,
+                                  device=dev),
+            }
 
     def build_stats(self, stream=None):
         wl = self.wl
@@ -220,6 +240,15 @@ class Decoder:
 
     def select(self, stream=None):
         b = self.buf
+        if self.superset:
+            wl, f = self.wl, self.first
+            select(self.shape, SEL_TOPK, wl.seq_lens, self.alpha, f["pages"], self.z, b.score, None, None,
+                   f["sel"], f["cnt"], None, b.ws_select, stream=stream)
+            entmax_decode(self.shape, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, f["sel"],
+                          f["cnt"], f["pages"], self.alpha, f["out"], f["tau"], f["ws"], stream=stream)
+            select(self.shape, SEL_SUPERSET, wl.seq_lens, self.alpha, self.budget, self.z, b.score, None, None,
+                   b.sel_pages, b.sel_count, f["tau"], b.ws_select, stream=stream)
+            return
         select(self.shape, self.selector, self.wl.seq_lens, self.alpha, self.budget, self.z, b.score, b.mu,
                b.sigma, b.sel_pages, b.sel_count, b.tau_hat, b.ws_select, stream=stream)
 

@@ -98,6 +98,23 @@ def test_select_argument_checks(lib):
                           None, None, ctypes.byref(n), None) == ekv.ERR_INVALID_ARG      # softmax + Gaussian
     assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_TOPK, None, 1.5, 8, 3.0, None, None, None, None, None,
                           None, None, None, None) == ekv.ERR_INVALID_ARG                 # no size pointer
+    assert lib.ekv_select(ctypes.byref(sh), ekv.SEL_SUPERSET, None, 1.0, 8, 3.0, None, None, None, None, None,
+                          None, None, ctypes.byref(n), None) == ekv.ERR_INVALID_ARG      # superset needs alpha > 1
+    assert lib.ekv_select(ctypes.byref(sh), 3, None, 1.5, 8, 3.0, None, None, None, None, None,
+                          None, None, ctypes.byref(n), None) == ekv.ERR_INVALID_ARG      # unknown selector
+
+
+def test_superset_select_needs_thresholds(lib):
+    """EKV_SEL_SUPERSET reads per-head lower bounds from tau_hat: a NULL
+    tau_hat is rejected before anything is launched."""
+    sh = _shape()
+    need = ekv.select_workspace_bytes(sh, ekv.SEL_SUPERSET, 1.5, 8)
+    assert need == ekv.select_workspace_bytes(sh, ekv.SEL_TOPK, 1.5, 8)
+    n = ctypes.c_size_t(need)
+    st = lib.ekv_select(ctypes.byref(sh), ekv.SEL_SUPERSET, 8, 1.5, 8, 3.0, 8, None, None, 8, 8, None, 256,
+                        ctypes.byref(n), None)
+    assert st == ekv.ERR_INVALID_ARG
+    assert b"tau_hat" in lib.ekv_last_error()
 
 
 def test_select_workspace_query(lib):

@@ -178,3 +178,50 @@ def test_generator_sentinel_and_layout():
     assert bool((tail == W.SENTINEL).all())
     used = wl.page_table[:, :M].reshape(-1).tolist()
     assert sorted(used) == list(range(wl.num_phys))
+
+
+@pytest.mark.parametrize("alpha", [4.0 / 3.0, 1.5, 2.0, 3.0])
+def test_threshold_of_a_subset_is_a_lower_bound(alpha):
+    """For any subset T of the tokens, sum_T [x - tau]_+^beta <= sum_all, so
+    the threshold solving the equation on T is at most the full threshold:
+    entmax over the tokens of any pages gives a conservative estimate for
+    the Appendix B.2 rule."""
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        n = int(rng.integers(2, 400))
+        s = rng.normal(size=n) * rng.uniform(0.2, 4.0)
+        _, tau_full, _ = em.entmax(s, alpha)
+        T = rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False)
+        _, tau_t, _ = em.entmax(s[T], alpha)
+        assert tau_t <= tau_full + 1e-12
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_superset_selector_pipeline_is_exact(alpha):
+    """Appendix B.2 end to end with a lower bound from a first pass: entmax
+    over the top-k0 pages by box score gives tau_lo <= tau per head; pages with
+    (alpha-1) U > min_h tau_lo then hold every support token of every head of
+    the group, so rho = 1, delta = 0 and the output equals the full-cache
+    output (Proposition 3.2)."""
+    for seed in range(4):
+        q, K, V = _problem(seed, n=900, G=2, H=4, d=16, scale=2.0)
+        n, P, G = K.shape[0], 16, 2
+        H = q.shape[0]
+        r = H // G
+        full = dec.decode(q, K, V, None, alpha)
+        kmin, kmax, _, _ = pg.page_stats(K, P)
+        _, U = pg.box_scores(q, kmin, kmax)
+        M = U.shape[1]
+        for g in range(G):
+            hs = slice(g * r, (g + 1) * r)
+            first = sel.topk_pages(U[g], 2)
+            toks = dec.tokens_of_pages(first, n, P)
+            tau_lo = dec.decode(q[hs], K[:, g:g + 1], V[:, g:g + 1], toks, alpha)["tau"]
+            assert np.all(tau_lo <= full["tau"][hs] + 1e-12)
+            pages = sel.superset_pages(U[g], tau_lo, alpha, M)
+            keep = dec.tokens_of_pages(pages, n, P)
+            sp = dec.decode(q[hs], K[:, g:g + 1], V[:, g:g + 1], keep, alpha)
+            sub_full = {"p": full["p"][hs], "out": full["out"][hs]}
+            m = dec.metrics(sub_full, sp, n)
+            assert np.all(m["rho"] == 1.0) and np.all(np.abs(m["delta"]) < 1e-12)
+            assert np.all(m["R"] < 1e-10)
