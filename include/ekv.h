@@ -111,6 +111,26 @@ ekv_status ekv_build_page_stats(const ekv_shape* shape, const void* k_cache,
                                 void* kmin, void* kmax, void* kmean, void* kvar,
                                 void* stream);
 
+/* Append one decoded token per sequence and refresh the statistics of the
+ * page it lands in (the step on the other side of the path: every decode
+ * step writes one key/value per sequence into the writable page, whose
+ * metadata must then cover it; [EKV] section 4.1 costs page metadata per page,
+ * and section 4.2 defines it).
+ *   k_new, v_new [B][G][D] kv_dtype: the new token's key and value per group.
+ *   For each sequence b with n = seq_lens[b]: the token is written at
+ *   logical position n (page n/P, slot n%P, through page_table, which must
+ *   already map that page); then the statistics of that page are recomputed
+ *   from its n%P + 1 tokens with the same arithmetic as ekv_build_page_stats,
+ *   so they equal a full rebuild bit for bit.  kmin/kmax and kmean/kvar may
+ *   each be NULL (in pairs) to skip them.
+ *   new_lens [B] int32 (NULL ok, must not alias seq_lens): n + 1, or n for a
+ *   sequence that was left untouched because page n/P is beyond the table
+ *   (n >= MP*P) or maps outside [0, NP).
+ * seq_lens itself is not modified.                                          */
+ekv_status ekv_append_kv(const ekv_shape* shape, const void* k_new, const void* v_new,
+                         const int32_t* page_table, const int32_t* seq_lens, void* k_cache, void* v_cache,
+                         void* kmin, void* kmax, void* kmean, void* kvar, int32_t* new_lens, void* stream);
+
 /* Query-aware page scores ([EKV] section 4.2 and Appendix B.1; section 4.3).
  * EKV_SEL_TOPK (reads kmin, kmax; writes score [B][G][MP] fp32):
  *   u_{h,p} = (1/sqrt(D)) sum_i max(q_{h,i} kmax_{p,i}, q_{h,i} kmin_{p,i}),
@@ -195,7 +215,7 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
 /* Message describing the last error returned on this thread ("" if none). */
 const char* ekv_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int32_t ekv_abi_version(void);
 
 #ifdef __cplusplus

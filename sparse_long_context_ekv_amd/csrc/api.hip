@@ -77,7 +77,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 extern "C" {
 
-int32_t ekv_abi_version(void) { return 1; }
+int32_t ekv_abi_version(void) { return 2; }
 
 const char* ekv_last_error(void) { return g_err; }
 
@@ -96,6 +96,24 @@ ekv_status ekv_build_page_stats(const ekv_shape* shape, const void* k_cache, con
     return hip_status(ekv::launch_page_stats(d, k_cache, page_table, seq_lens, page_list, n_list, kmin, kmax,
                                              kmean, kvar, (hipStream_t)stream),
                       "ekv_build_page_stats");
+}
+
+ekv_status ekv_append_kv(const ekv_shape* shape, const void* k_new, const void* v_new,
+                         const int32_t* page_table, const int32_t* seq_lens, void* k_cache, void* v_cache,
+                         void* kmin, void* kmax, void* kmean, void* kvar, int32_t* new_lens, void* stream) {
+    ekv::Dims d;
+    ekv_status st = check_shape(shape, &d);
+    if (st != EKV_OK) return st;
+    if (!k_new || !v_new || !page_table || !seq_lens || !k_cache || !v_cache)
+        return fail(EKV_ERR_INVALID_ARG, "k_new, v_new, page_table, seq_lens, k_cache and v_cache are required");
+    if ((kmin == nullptr) != (kmax == nullptr)) return fail(EKV_ERR_INVALID_ARG, "kmin and kmax must both be given or both NULL");
+    if ((kmean == nullptr) != (kvar == nullptr)) return fail(EKV_ERR_INVALID_ARG, "kmean and kvar must both be given or both NULL");
+    if (new_lens && (const void*)new_lens == (const void*)seq_lens)
+        return fail(EKV_ERR_INVALID_ARG, "new_lens must not alias seq_lens");
+    if ((long long)d.B * d.MP > 0x7fffffffLL) return fail(EKV_ERR_UNSUPPORTED, "batch*max_pages too large");
+    return hip_status(ekv::launch_append_kv(d, k_new, v_new, page_table, seq_lens, k_cache, v_cache, kmin, kmax,
+                                            kmean, kvar, new_lens, (hipStream_t)stream),
+                      "ekv_append_kv");
 }
 
 ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void* q, const int32_t* page_table,

@@ -20,6 +20,11 @@ hipError_t launch_page_stats(const Dims& d, const void* k_cache, const int32_t* 
                              const int32_t* seq_lens, const int32_t* page_list, int n_list,
                              void* kmin, void* kmax, void* kmean, void* kvar, hipStream_t s);
 
+// Append one token per sequence (+ statistics of its page).
+hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new, const int32_t* page_table,
+                            const int32_t* seq_lens, void* k_cache, void* v_cache, void* kmin, void* kmax,
+                            void* kmean, void* kvar, int32_t* new_lens, hipStream_t s);
+
 // Page scores.
 hipError_t launch_box_score(const Dims& d, const void* q, const int32_t* page_table,
                             const int32_t* seq_lens, const void* kmin, const void* kmax,

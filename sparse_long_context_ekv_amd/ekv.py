@@ -25,7 +25,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 SEL_TOPK, SEL_GAUSS, SEL_SUPERSET = 0, 1, 2
 _STATUS = {0: "EKV_OK", 1: "EKV_ERR_INVALID_ARG", 2: "EKV_ERR_UNSUPPORTED", 3: "EKV_ERR_WORKSPACE", 4: "EKV_ERR_HIP"}
-SYMBOLS = ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
+SYMBOLS = ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
            "ekv_last_error", "ekv_abi_version")
 
 
@@ -59,11 +59,12 @@ def load(path: str | None = None):
     lib = ctypes.CDLL(p)
     sp = ctypes.POINTER(Shape)
     lib.ekv_build_page_stats.argtypes = [sp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.ekv_append_kv.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_score_pages.argtypes = [sp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_select.argtypes = [sp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _szp, _vp]
-    for name in ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
+    for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ekv_last_error.restype = ctypes.c_char_p
     lib.ekv_last_error.argtypes = []
@@ -109,6 +110,13 @@ def build_page_stats(shape, k_cache, page_table, seq_lens, kmin=None, kmax=None,
     _check(load().ekv_build_page_stats(ctypes.byref(shape), _ptr(k_cache), _ptr(page_table), _ptr(seq_lens),
                                        _ptr(page_list), n_list, _ptr(kmin), _ptr(kmax), _ptr(kmean),
                                        _ptr(kvar), _stream(stream)))
+
+
+def append_kv(shape, k_new, v_new, page_table, seq_lens, k_cache, v_cache, kmin=None, kmax=None, kmean=None,
+              kvar=None, new_lens=None, stream=None):
+    _check(load().ekv_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(page_table), _ptr(seq_lens),
+                                _ptr(k_cache), _ptr(v_cache), _ptr(kmin), _ptr(kmax), _ptr(kmean), _ptr(kvar),
+                                _ptr(new_lens), _stream(stream)))
 
 
 def score_pages(shape, selector, q, page_table, seq_lens, kmin=None, kmax=None, kmean=None, kvar=None,

@@ -30,14 +30,14 @@ def lib():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for n in ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
+    for n in ("ekv_build_page_stats", "ekv_score_pages", "ekv_select", "ekv_entmax_decode", "ekv_append_kv"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ekv_abi_version() == 1
+    assert lib.ekv_abi_version() == 2
 
 
 def _shape(**kw):
@@ -153,3 +153,16 @@ def test_decode_workspace_query_and_checks(lib):
     st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, 8, 8, None, None, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # sel_pages without sel_count
+
+
+def test_append_argument_checks(lib):
+    """ekv_append_kv rejects missing buffers, unpaired statistics and an
+    output length array that aliases the input lengths, before launching."""
+    sh = _shape()
+    a = ctypes.byref(sh)
+    assert lib.ekv_append_kv(a, None, 8, 8, 8, 8, 8, None, None, None, None, None, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_append_kv(a, 8, 8, 8, 8, 8, 8, 8, None, None, None, None, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_append_kv(a, 8, 8, 8, 8, 8, 8, None, None, 8, None, None, None) == ekv.ERR_INVALID_ARG
+    st = lib.ekv_append_kv(a, 8, 8, 8, 1024, 8, 8, None, None, None, None, 1024, None)
+    assert st == ekv.ERR_INVALID_ARG and b"alias" in lib.ekv_last_error()
+    assert lib.ekv_append_kv(None, 8, 8, 8, 8, 8, 8, None, None, None, None, None, None) == ekv.ERR_INVALID_ARG
