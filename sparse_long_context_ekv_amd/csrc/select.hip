@@ -91,31 +91,29 @@ __device__ __forceinline__ void gauss_terms(float m, float v, float& e_b, float&
     }
 }
 
-// Sums over this thread's pages among every S-th page p = 0, S, 2S, ...:
-// f += w_p e_beta, d1 += w_p e_(beta-1), d2 += w_p e_(beta-2), w_p = S n_p
-// (S = 1: every page with its own weight; S > 1: a subsample standing for
-// the whole sequence).  Two pages per trip; only the last page is partial.
+// Sums over pages p = first, first + step, ... < count of `src`:
+// f += w_p e_beta, d1 += w_p e_(beta-1), d2 += w_p e_(beta-2), with w_p = w
+// except for index `last`, which weighs w_last.  Two pages per trip.
 template <int BETA, bool STAGED>
-__device__ __forceinline__ void gauss_sums(const float2* __restrict__ lds2, const float* __restrict__ mrow,
-                                           const float* __restrict__ srow, int M, int S, float a, float last_np,
-                                           float t, float& f, float& d1, float& d2) {
-    const float wS = (float)(S * kPage);
+__device__ __forceinline__ void gauss_sums(const float2* __restrict__ src, const float* __restrict__ mrow,
+                                           const float* __restrict__ srow, int first, int step, int count,
+                                           int last, float w, float w_last, float a, float t, float& f, float& d1,
+                                           float& d2) {
     auto page = [&](int p) {
-        const float2 e = STAGED ? lds2[p] : make_float2(a * mrow[p], a * srow[p]);
-        const float w = (p == M - 1) ? (float)S * last_np : wS;
+        const float2 e = STAGED ? src[p] : make_float2(a * mrow[p], a * srow[p]);
+        const float wp = (p == last) ? w_last : w;
         float eb, eb1, eb2;
         gauss_terms<BETA>(e.x - t, e.y, eb, eb1, eb2);
-        f = fmaf(w, eb, f);
-        d1 = fmaf(w, eb1, d1);
-        d2 = fmaf(w, eb2, d2);
+        f = fmaf(wp, eb, f);
+        d1 = fmaf(wp, eb1, d1);
+        d2 = fmaf(wp, eb2, d2);
     };
-    const int step = S * kTauThreads;
-    int p = S * (int)threadIdx.x;
-    for (; p + step < M; p += 2 * step) {
+    int p = first;
+    for (; p + step < count; p += 2 * step) {
         page(p);
         page(p + step);
     }
-    if (p < M) page(p);
+    if (p < count) page(p);
 }
 
 // Root of F(tau) = 1 for one (sequence, head).  Every iteration evaluates,
@@ -132,56 +130,67 @@ __device__ __forceinline__ void gauss_sums(const float2* __restrict__ lds2, cons
 // times the Newton step on F^(1/beta), which is convex (an L^beta norm of
 // (Y - tau)_+ over the page mixture) and so never passes the root.  A step
 // that leaves the bracket is replaced by its midpoint.
-template <int BETA>
-__device__ float gauss_tau_solve(const float2* __restrict__ lds2, const float* __restrict__ mrow,
-                                 const float* __restrict__ srow, bool staged, int M, int S, float a,
-                                 float last_np, float lo, float t, float tol, float* red, int& phase) {
+// WAVE: one wave runs the whole iteration with wave-level sums and no block
+// barrier; otherwise the block shares the pages and sums across waves.
+template <int BETA, bool WAVE, bool STAGED>
+__device__ float gauss_tau_solve(const float2* __restrict__ src, const float* __restrict__ mrow,
+                                 const float* __restrict__ srow, int count, int last, float w, float w_last,
+                                 float a, float lo, float t, float tol, float* red, int& phase) {
     constexpr float fb = (float)BETA;
     float hi = INFINITY;
+    const int first = WAVE ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    const int step = WAVE ? 64 : kTauThreads;
     for (int it = 0; it < kTauMaxIter; ++it) {
         float f = 0.0f, d1 = 0.0f, d2 = 0.0f;
-        if (staged) gauss_sums<BETA, true>(lds2, mrow, srow, M, S, a, last_np, t, f, d1, d2);
-        else        gauss_sums<BETA, false>(lds2, mrow, srow, M, S, a, last_np, t, f, d1, d2);
-        block_sum3<kTauWaves>(f, d1, d2, red, phase);   // block-uniform from here on
+        gauss_sums<BETA, STAGED>(src, mrow, srow, first, step, count, last, w, w_last, a, t, f, d1, d2);
+        if constexpr (WAVE) {
+            f = wave_sum(f);
+            d1 = wave_sum(d1);
+            d2 = wave_sum(d2);
+        } else {
+            block_sum3<kTauWaves>(f, d1, d2, red, phase);   // block-uniform from here on
+        }
         if (f >= 1.0f) lo = fmaxf(lo, t); else hi = fminf(hi, t);
         if (f == 1.0f) break;
-        float step = NAN;
+        float step_t = NAN;
         if (d1 > 0.0f && f > 0.0f) {
             const float L = logf(f);
             const float dL = -fb * d1 / f;                      // d log F / d tau
-            step = -L / dL;
+            step_t = -L / dL;
             if constexpr (BETA >= 2) {
                 const float d2L = fb * (fb - 1.0f) * d2 / f - dL * dL;
                 const float den = 2.0f * dL * dL - L * d2L;
-                if (den > 0.0f) step = -2.0f * L * dL / den;
+                if (den > 0.0f) step_t = -2.0f * L * dL / den;
             }
             if (f > 1.0f) {
                 const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
-                step = fminf(step, 4.0f * (1.0f - 1.0f / gr) * f / d1);
+                step_t = fminf(step_t, 4.0f * (1.0f - 1.0f / gr) * f / d1);
             }
         }
-        float nt = t + step;
+        float nt = t + step_t;
         if (!(nt >= lo && nt <= hi)) {
             if (!(hi < INFINITY) || !(lo > -INFINITY)) break;   // no usable step, no finite bracket
             nt = 0.5f * (lo + hi);
-            step = nt - t;
+            step_t = nt - t;
         }
-        const bool done = fabsf(step) <= tol * fmaxf(1.0f, fabsf(t));
+        const bool done = fabsf(step_t) <= tol * fmaxf(1.0f, fabsf(t));
         t = nt;
         if (done) break;
     }
     return t;
 }
 
-// One block per (sequence, head).  The iteration first runs on every 16th
-// page (weights x16) to a loose tolerance, and the passes over all pages start
-// from that estimate: 2 to 3 full passes instead of 5 to 6 on 8192-page
-// sequences.  The full passes keep the exact lower end max_p (alpha-1) mu_p - 1.
+// One block per (sequence, head).  Staging copies (a mu, a sigma) of every
+// page into LDS (16-byte loads) and every kTauSub-th page into a compact
+// array; the iteration first runs on that subsample (weights x kTauSub, in
+// one wave) to a loose tolerance, and the passes over all pages start
+// from its estimate: 2 full passes instead of 5 to 6 on 8192-page sequences.
+// The full passes keep the exact lower end max_p (alpha-1) mu_p - 1.
 template <int BETA>
 __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
     const float* __restrict__ mu, const float* __restrict__ sigma, const int32_t* __restrict__ seq_lens,
     int HQ, int MP, float a, int lds_pages, float* __restrict__ tau_hat) {
-    extern __shared__ float2 lds2[];               // [lds_pages] (a*mu, a*sigma) when staged
+    extern __shared__ float2 lds2[];               // [lds_pages] pages, then [lds_pages / kTauSub] subsample
     __shared__ float red[6 * kTauWaves];
     int phase = 0;
     const int h = blockIdx.x, b = blockIdx.y;
@@ -196,20 +205,63 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
     const float* mrow = mu + ((size_t)b * HQ + h) * MP;
     const float* srow = sigma + ((size_t)b * HQ + h) * MP;
     const bool staged = M <= lds_pages;
+    float2* sub2 = lds2 + lds_pages;
+    const int msub = (M + kTauSub - 1) / kTauSub;
 
     float xmax = -INFINITY;
-    for (int p = threadIdx.x; p < M; p += kTauThreads) {
-        const float xm = a * mrow[p];
-        xmax = fmaxf(xmax, xm);
-        if (staged) lds2[p] = make_float2(xm, a * srow[p]);
+    const bool vec = staged && ((((uintptr_t)mrow) | ((uintptr_t)srow)) & 15) == 0;
+    if (vec) {
+        for (int p4 = 4 * (int)threadIdx.x; p4 < M; p4 += 4 * kTauThreads) {
+            if (p4 + 4 <= M) {
+                const float4 m4 = *reinterpret_cast<const float4*>(mrow + p4);
+                const float4 s4 = *reinterpret_cast<const float4*>(srow + p4);
+                const float xm[4] = {a * m4.x, a * m4.y, a * m4.z, a * m4.w};
+                const float xs[4] = {a * s4.x, a * s4.y, a * s4.z, a * s4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xmax = fmaxf(xmax, xm[i]);
+                    lds2[p4 + i] = make_float2(xm[i], xs[i]);
+                    if (((p4 + i) & (kTauSub - 1)) == 0) sub2[(p4 + i) / kTauSub] = make_float2(xm[i], xs[i]);
+                }
+            } else {
+                for (int p = p4; p < M; ++p) {
+                    const float xm = a * mrow[p];
+                    xmax = fmaxf(xmax, xm);
+                    lds2[p] = make_float2(xm, a * srow[p]);
+                    if ((p & (kTauSub - 1)) == 0) sub2[p / kTauSub] = lds2[p];
+                }
+            }
+        }
+    } else {
+        for (int p = threadIdx.x; p < M; p += kTauThreads) {
+            const float xm = a * mrow[p];
+            xmax = fmaxf(xmax, xm);
+            if (staged) {
+                lds2[p] = make_float2(xm, a * srow[p]);
+                if ((p & (kTauSub - 1)) == 0) sub2[p / kTauSub] = lds2[p];
+            }
+        }
     }
     xmax = block_max<kTauWaves>(xmax, red, phase);   // barrier also publishes LDS
     const float lo = xmax - 1.0f;                    // F(lo) >= 1 (Jensen on the top page)
     float t = lo;
-    if (M >= kTauSubMin)                             // no lower end known for the subsample
-        t = gauss_tau_solve<BETA>(lds2, mrow, srow, staged, M, kTauSub, a, last_np, -INFINITY, lo,
-                                  kTauSubTol, red, phase);
-    t = gauss_tau_solve<BETA>(lds2, mrow, srow, staged, M, 1, a, last_np, lo, t, kTauTol, red, phase);
+    const float wsub = (float)(kTauSub * kPage);
+    if (staged && M >= kTauSubMin) {                 // no lower end known for the subsample
+        __shared__ float sh_t;
+        if (threadIdx.x < 64) {                      // wave 0 alone; the others wait at the barrier
+            const float ts = gauss_tau_solve<BETA, true, true>(sub2, mrow, srow, msub, -1, wsub, wsub, a,
+                                                               -INFINITY, lo, kTauSubTol, red, phase);
+            if (threadIdx.x == 0) sh_t = ts;
+        }
+        __syncthreads();
+        t = sh_t;
+    }
+    if (staged)
+        t = gauss_tau_solve<BETA, false, true>(lds2, mrow, srow, M, M - 1, (float)kPage, last_np, a, lo, t,
+                                               kTauTol, red, phase);
+    else
+        t = gauss_tau_solve<BETA, false, false>(lds2, mrow, srow, M, M - 1, (float)kPage, last_np, a, lo, t,
+                                                kTauTol, red, phase);
     if (threadIdx.x == 0) *out = t;
 }
 
@@ -584,7 +636,7 @@ static hipError_t run_gauss_tau(const Dims& d, const float* mu, const float* sig
     static bool attr_ok[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    const size_t max_lds = (size_t)kTauLdsPages * sizeof(float2);
+    const size_t max_lds = (size_t)(kTauLdsPages + kTauLdsPages / kTauSub) * sizeof(float2);
     if (!attr_ok[dev]) {
         if (hipFuncSetAttribute((const void*)gauss_tau_kernel<BETA>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)max_lds) == hipSuccess)
@@ -592,9 +644,12 @@ static hipError_t run_gauss_tau(const Dims& d, const float* mu, const float* sig
         else
             (void)hipGetLastError();
     }
+    // lds_pages is a multiple of kTauSub: the subsample array follows the pages.
     int lds_pages = attr_ok[dev] ? (d.MP < kTauLdsPages ? d.MP : kTauLdsPages) : 0;
-    if (!attr_ok[dev] && (size_t)d.MP * sizeof(float2) <= 48 * 1024) lds_pages = d.MP;
-    gauss_tau_kernel<BETA><<<dim3(d.HQ, d.B), dim3(kTauThreads), (size_t)lds_pages * sizeof(float2), s>>>(
+    if (!attr_ok[dev] && (size_t)d.MP * sizeof(float2) * (kTauSub + 1) / kTauSub <= 48 * 1024) lds_pages = d.MP;
+    lds_pages = (lds_pages + kTauSub - 1) / kTauSub * kTauSub;
+    const size_t lds = (size_t)(lds_pages + lds_pages / kTauSub) * sizeof(float2);
+    gauss_tau_kernel<BETA><<<dim3(d.HQ, d.B), dim3(kTauThreads), lds, s>>>(
         mu, sigma, seq_lens, d.HQ, d.MP, a, lds_pages, tau_hat);
     return hipGetLastError();
 }
