@@ -14,11 +14,13 @@
 // Both kernels are pure streams over the page statistics: one 16-lane row
 // per (page, group), lane l owning channels [l*CH, (l+1)*CH), the r query
 // slices of the group in registers, one fixed-order DPP row sum per head.
-// A block covers 2^lg_ppb consecutive logical pages of one sequence; each row
-// issues the loads of UNROLL pages before using any of them.  Results are
-// staged in LDS and written once per block, one contiguous run of pages per
-// output row: single-float stores scattered over the [B][.][MP] rows (one per
-// page and head) cost more HBM time than the whole statistics stream saves.
+// A block covers 2^lg_ppb consecutive logical pages of one sequence (up to
+// 256); each row issues the loads of UNROLL pages before using any of them.
+// Results are staged in LDS and written once, at the end of the block, one
+// contiguous run of pages per output row: single-float stores scattered over
+// the [B][.][MP] rows (one per page and head) cost the statistics stream a
+// third of its speed, and stores interleaved with the stream cost twice what
+// they cost alone.
 #include "ekv_device.h"
 #include "ekv_internal.h"
 
@@ -198,19 +200,39 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
     }
 }
 
-// log2 of the pages per block: 16 (measured best on the 128K batched
-// workload), fewer when that leaves under ~2048 blocks for 256 CUs.
-static int score_lg_ppb(const Dims& d) {
+// log2 of the pages per block.  Measured on the 128K batched workload: with
+// fp32 statistics (1 KiB per page and group) 256-page blocks, whose staged
+// outputs go out in long runs at the end, beat 16-page blocks by ~3%; with
+// 16-bit statistics (half the bytes per page) the 512 large blocks keep too
+// few loads in flight and 16-page blocks are 25% faster.  Fewer pages when
+// that leaves under 512 blocks for 256 CUs or the block's outputs
+// (`out_per_page` floats per page) would pass 64 KiB of LDS.
+static int score_lg_ppb(const Dims& d, int out_per_page, int lg_max) {
     const long units = (long)d.B * d.MP;
-    int lg = 4;
-    while (lg > 2 && (units >> lg) < 2048) --lg;
+    int lg = lg_max;
+    while (lg > 2 && ((units >> lg) < 512 || ((long)out_per_page << lg) * 4 > 65536)) --lg;
     return lg;
+}
+
+template <typename K>
+static bool allow_64k_lds(K kernel) {
+    static bool ok[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!ok[dev]) {
+        if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 65536) == hipSuccess)
+            ok[dev] = true;
+        else
+            (void)hipGetLastError();
+    }
+    return ok[dev];
 }
 
 template <typename T, int D, int R>
 static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                           const void* kmin, const void* kmax, float* score, hipStream_t s) {
-    const int lg = score_lg_ppb(d);
+    int lg = score_lg_ppb(d, d.G, d.kv_bf16 ? 4 : 8);
+    if (((size_t)d.G << lg) * sizeof(float) > 48 * 1024 && !allow_64k_lds(box_score_kernel<T, D, R>)) lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
     const size_t lds = ((size_t)d.G << lg) * sizeof(float);
     box_score_kernel<T, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const T*)kmin, (const T*)kmax,
@@ -221,7 +243,9 @@ static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const
 template <typename T, typename S, int D, int R>
 static hipError_t run_gauss(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                             const void* kmean, const void* kvar, float* mu, float* sigma, hipStream_t s) {
-    const int lg = score_lg_ppb(d);
+    int lg = score_lg_ppb(d, 2 * d.HQ, d.stat_bf16 ? 4 : 8);
+    if (((size_t)2 * d.HQ << lg) * sizeof(float) > 48 * 1024 && !allow_64k_lds(gauss_score_kernel<T, S, D, R>))
+        lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
     const size_t lds = ((size_t)2 * d.HQ << lg) * sizeof(float);
     gauss_score_kernel<T, S, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const S*)kmean,
