@@ -468,13 +468,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Wave-wide sum of an int (any order is exact).
-__device__ __forceinline__ int wave_isum(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 template <int MODE>
 __device__ __forceinline__ float pw(float d, float beta) {      // d^beta, d > 0
     return MODE == kModeBeta1 ? d : (MODE == kModeBeta2 ? d * d : powf(d, beta));
@@ -484,49 +477,58 @@ __device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d
     return MODE == kModeBeta1 ? 1.0f : (MODE == kModeBeta2 ? d : powf(d, beta - 1.0f));
 }
 
-// One block per (sequence, KV group) with one wave per query head of the
-// group; the waves never synchronise with each other.  Wave j:
-//  0. stages the physical page of every selected page in LDS (its loads
-//     overlap the logits loads);
-//  1. holds x = (alpha-1) s of its head's selected slots in registers
-//     (slot k*256 + 4*lane + c in xr[k][c]), invalid slots -inf;
-//  2. compacts the threshold candidates x > max(x) - 1 (only those can be in
-//     the support: the top term alone is at most 1) with their slots into
-//     LDS, lane by lane after one wave scan of per-lane counts (a fixed
-//     order, so results are reproducible); past kCandLds candidates it keeps
-//     working on the registers;
-//  3. finds tau from sum [x - tau]_+^beta = 1 by Newton steps on
-//     F^(1/beta) from tau = max(x) - 1: for beta >= 1 this is the L^beta norm
-//     of (x - tau)_+, convex and decreasing, so the steps rise monotonically
-//     without passing the root (beta < 1: bisection); for beta in {1, 2} the
-//     closed form on the support found then gives tau exactly;
-//  4. writes tau, the support size and the dropped mass w.r.t. tau_ref
-//     (tau_ref, the threshold over a superset of these tokens, is at least
-//     max(x) - 1, so only candidates contribute);
-//  5. compacts its support (slot, p = [x - tau]_+^beta) and gathers only
-//     those V rows, four per step across the 16-lane rows, summing p v in a
-//     fixed order.
-template <typename T, int D, int R, int KPL, int MODE>
-__global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
+// One block per (sequence, KV group): the r query heads of the group, each
+// split over W waves (W = 16 / r, at most the register chunks available), so
+// a wave holds KPLW float4 of logits per lane; slot k*256 + 4*lane + c of the
+// wave's part sits in xr[k][c], invalid slots -inf.  Per head:
+//  0. the block stages the physical page of every selected page in LDS (its
+//     loads overlap the logits loads);
+//  1. max(x) over the head's waves (x = (alpha-1) s);
+//  2. each wave compacts its threshold candidates x > max(x) - 1 (only those
+//     can be in the support: the top term alone is at most 1) with their
+//     slots into its own LDS list, lane by lane after one wave scan of
+//     per-lane counts (a fixed order, so results are reproducible); past CW
+//     candidates the wave keeps working on its registers;
+//  3. tau from sum [x - tau]_+^beta = 1 by Newton steps on F^(1/beta) from
+//     tau = max(x) - 1: for beta >= 1 this is the L^beta norm of (x - tau)_+,
+//     convex and decreasing, so the steps rise monotonically without passing
+//     the root (beta < 1: bisection).  Each iteration sums per wave, and the
+//     head's W partials are added in a fixed order after one block barrier
+//     (partials double-buffered); for beta in {1, 2} the closed form on the
+//     support found then gives tau exactly;
+//  4. tau, the support size and the dropped mass w.r.t. tau_ref (tau_ref,
+//     the threshold over a superset of these tokens, is at least max(x) - 1,
+//     so only candidates contribute);
+//  5. each wave compacts its part of the support (slot, p = [x - tau]_+^beta)
+//     and gathers only those V rows, four per step across the 16-lane rows;
+//     the W partial outputs are summed in a fixed order.
+template <typename T, int D, int R, int W, int KPLW, int MODE>
+__global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
     int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
     float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
     float* __restrict__ delta_out) {
+    constexpr int NWV = R * W;                   // waves in the block
     constexpr int CH = D / kRow;
     constexpr int PVU = 4;                       // V rows per 16-lane row in flight
-    constexpr int NPG = KPL * 256 / kPage;       // selected pages per head at most
-    __shared__ float cand_x[R][kCandLds + 64];   // + one dump slot per lane
-    __shared__ int cand_s[R][kCandLds + 64];
-    __shared__ int pv_slot[R][kPvList + 64];
-    __shared__ float pv_p[R][kPvList + 64];
-    __shared__ int phys_of[R][NPG];
+    constexpr int NPG = W * KPLW * 256 / kPage;  // selected pages per head at most
+    constexpr int CW = kCandLds / W;             // candidates per wave kept in LDS
+    constexpr int PW = kPvList / W;              // support entries per wave per pass
+    __shared__ float cand_x[NWV][CW + 64];       // + one dump slot per lane
+    __shared__ int cand_s[NWV][CW + 64];
+    __shared__ int pv_slot[NWV][PW + 64];
+    __shared__ float pv_p[NWV][PW + 64];
+    __shared__ int phys_of[NPG];
+    __shared__ float part[2][NWV][4];
+    __shared__ int flag[2][NWV];
+    __shared__ float pvout[NWV][D];
     const int unit = blockIdx.x;
     const int b = unit / G, g = unit - b * G;
     const int HQ = G * R;
-    const int j = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = wv / W, w = wv - j * W;
     const size_t oh = (size_t)b * HQ + g * R + j;
     const int n = seq_len_at(seq_lens, b, MP);
     const int M = num_pages(n);
@@ -534,22 +536,24 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
     const int nused = cnt * kPage;
     const size_t nslot = (size_t)sel_stride * kPage;
     const float a = alpha - 1.0f;
+    const int base = w * KPLW * 256;             // first slot of this wave's part
     const float* lrow = logits + oh * nslot;
     float* o = out + oh * D;
 
-    // 0. selected logical pages (loads issued first), then the logits
+    // 0. selected logical pages -> physical pages (loads first), then the logits
     const int32_t* sel = sel_pages + (size_t)unit * sel_stride;
-    constexpr int NPL = (NPG + 63) / 64;
+    const int32_t* pt = page_table + (size_t)b * MP;
+    constexpr int NPL = (NPG + 64 * NWV - 1) / (64 * NWV);
     int lpg[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-        const int ip = i * 64 + lane;
+        const int ip = i * 64 * NWV + (int)threadIdx.x;
         lpg[i] = ip < cnt ? sel[ip] : -1;
     }
-    float xr[KPL][4];
+    float xr[KPLW][4];
 #pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-        const int s0 = k * 256 + 4 * lane;
+    for (int k = 0; k < KPLW; ++k) {
+        const int s0 = base + k * 256 + 4 * lane;
         float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         if (s0 < nused) v = *reinterpret_cast<const float4*>(lrow + s0);
         xr[k][0] = v.x;
@@ -557,111 +561,150 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
         xr[k][2] = v.z;
         xr[k][3] = v.w;
     }
-    const int32_t* pt = page_table + (size_t)b * MP;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-        const int ip = i * 64 + lane;
+        const int ip = i * 64 * NWV + (int)threadIdx.x;
         if (ip < NPG) {
             const int lp = lpg[i];
             const int ph = (lp >= 0 && lp < M) ? pt[lp] : -1;
-            phys_of[j][ip] = (ph >= 0 && ph < NP) ? ph : -1;
+            phys_of[ip] = (ph >= 0 && ph < NP) ? ph : -1;
         }
     }
 
-    float xmax = -INFINITY;
-    int nvalid = 0;
+    // 1. max over the head (and the valid count, for the bisection bracket)
+    float xm = -INFINITY;
+    int nv = 0;
 #pragma unroll
-    for (int k = 0; k < KPL; ++k)
+    for (int k = 0; k < KPLW; ++k)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             xr[k][c] *= a;
-            xmax = fmaxf(xmax, xr[k][c]);
-            nvalid += xr[k][c] > -INFINITY ? 1 : 0;
+            xm = fmaxf(xm, xr[k][c]);
+            nv += xr[k][c] > -INFINITY ? 1 : 0;
         }
-    xmax = wave_max(xmax);
-    if (!(xmax > -INFINITY)) {                   // empty candidate set (wave-uniform)
-        for (int c = lane; c < D; c += 64) o[c] = 0.0f;
-        if (lane == 0) {
-            tau_out[oh] = -INFINITY;
-            if (support_out) support_out[oh] = 0;
-            if (delta_out) delta_out[oh] = 1.0f;
-        }
-        return;
+    xm = wave_max(xm);
+    nv = wave_isum(nv);
+    if (lane == 0) {
+        part[0][wv][0] = xm;
+        part[0][wv][1] = (float)nv;
     }
-    nvalid = wave_isum(nvalid);
-    const float lo = xmax - 1.0f;
+    __syncthreads();
+    float xmax = -INFINITY, nvalid = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+        xmax = fmaxf(xmax, part[0][j * W + w2][0]);
+        nvalid += part[0][j * W + w2][1];
+    }
+    // A head without a finite logit (no valid slot, or non-finite inputs) does
+    // no work but still takes part in every barrier below.
+    const bool empty = !(xmax > -INFINITY);
+    const float lo = empty ? 0.0f : xmax - 1.0f;
 
-    // 2. candidates x > lo
+    // 2. this wave's candidates x > lo
     int mine = 0;
 #pragma unroll
-    for (int k = 0; k < KPL; ++k)
+    for (int k = 0; k < KPLW; ++k)
 #pragma unroll
         for (int c = 0; c < 4; ++c) mine += xr[k][c] > lo ? 1 : 0;
     const int incl = wave_incl_scan(mine);
-    const int ncand = __shfl(incl, 63, 64);
-    const bool in_lds = ncand <= kCandLds;
-    float* cx = cand_x[j];
-    int* cs = cand_s[j];
+    const int ncand = __builtin_amdgcn_readlane(incl, 63);
+    const bool in_lds = ncand <= CW;
+    float* cx = cand_x[wv];
+    int* cs = cand_s[wv];
     if (in_lds) {
         int pos = incl - mine;
-        const int dump = kCandLds + lane;
+        const int dump = CW + lane;
 #pragma unroll
-        for (int k = 0; k < KPL; ++k)
+        for (int k = 0; k < KPLW; ++k)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const bool f = xr[k][c] > lo;
                 const int at = f ? pos : dump;
                 cx[at] = xr[k][c];
-                cs[at] = k * 256 + 4 * lane + c;
+                cs[at] = base + k * 256 + 4 * lane + c;
                 pos += f ? 1 : 0;
             }
         wave_lds_sync();
     }
-    // Visit every candidate (x, slot) this lane owns.
     auto each_cand = [&](auto&& fn) {
         if (in_lds) {
             for (int i = lane; i < ncand; i += 64) fn(cx[i], cs[i]);
         } else {
 #pragma unroll
-            for (int k = 0; k < KPL; ++k)
+            for (int k = 0; k < KPLW; ++k)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    if (xr[k][c] > lo) fn(xr[k][c], k * 256 + 4 * lane + c);
+                    if (xr[k][c] > lo) fn(xr[k][c], base + k * 256 + 4 * lane + c);
         }
+    };
+    // Sum of the head's W wave partials (fixed order), after a barrier.
+    int pb = 1;
+    auto head_sums = [&](float v0, float v1, float v2, float v3, int fl, float* r, bool& any) {
+        pb ^= 1;
+        if (lane == 0) {
+            part[pb][wv][0] = v0;
+            part[pb][wv][1] = v1;
+            part[pb][wv][2] = v2;
+            part[pb][wv][3] = v3;
+            flag[pb][wv] = fl;
+        }
+        __syncthreads();
+        r[0] = r[1] = r[2] = r[3] = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] += part[pb][j * W + w2][i];
+        any = false;
+#pragma unroll
+        for (int v2 = 0; v2 < NWV; ++v2) any = any || flag[pb][v2] != 0;
     };
 
     // 3. tau
-    auto sums = [&](float t, float& f, float& df) {
-        float s1 = 0.0f, s0 = 0.0f;
-        each_cand([&](float x, int) {
-            const float d = x - t;
-            if (d > 0.0f) {
-                s1 += pw<MODE>(d, beta);
-                s0 += pw1<MODE>(d, beta);
-            }
-        });
-        f = wave_sum(s1);
-        df = wave_sum(s0);
-    };
     float tau = lo;
     if (MODE != kModeGeneral || beta >= 1.0f) {
+        bool active = !empty;
         for (int it = 0; it < 100; ++it) {
-            float f, df;
-            sums(tau, f, df);
-            if (!(f > 1.0f) || !(df > 0.0f)) break;
-            const float gr = MODE == kModeBeta1 ? f : (MODE == kModeBeta2 ? sqrtf(f) : powf(f, 1.0f / beta));
-            const float nt = tau + (1.0f - 1.0f / gr) * f / df;
-            if (!(nt > tau)) break;
-            tau = nt;
+            float s1 = 0.0f, s0 = 0.0f;
+            if (active)
+                each_cand([&](float x, int) {
+                    const float d = x - tau;
+                    if (d > 0.0f) {
+                        s1 += pw<MODE>(d, beta);
+                        s0 += pw1<MODE>(d, beta);
+                    }
+                });
+            s1 = wave_sum(s1);
+            s0 = wave_sum(s0);
+            float r[4];
+            bool any;
+            head_sums(s1, s0, 0.0f, 0.0f, active ? 1 : 0, r, any);
+            if (!any) break;                                 // block-uniform
+            if (active) {
+                const float f = r[0], df = r[1];
+                if (!(f > 1.0f) || !(df > 0.0f)) {
+                    active = false;
+                } else {
+                    const float gr = MODE == kModeBeta1 ? f : (MODE == kModeBeta2 ? sqrtf(f) : powf(f, 1.0f / beta));
+                    const float nt = tau + (1.0f - 1.0f / gr) * f / df;
+                    if (!(nt > tau)) active = false; else tau = nt;
+                }
+            }
         }
     } else {
         // beta < 1 (alpha > 2): bisection on [max - 1, max - n^(1-alpha)]
-        float l2 = lo, hi = xmax - powf((float)nvalid, 1.0f - alpha);
+        float l2 = lo, hi = xmax - powf(nvalid, 1.0f - alpha);
         for (int it = 0; it < 60; ++it) {
             const float mid = 0.5f * (l2 + hi);
-            float f, df;
-            sums(mid, f, df);
-            if (f >= 1.0f) l2 = mid; else hi = mid;
+            float s1 = 0.0f;
+            each_cand([&](float x, int) {
+                const float d = x - mid;
+                if (d > 0.0f) s1 += pw<MODE>(d, beta);
+            });
+            s1 = wave_sum(s1);
+            float r[4];
+            bool any;
+            head_sums(s1, 0.0f, 0.0f, 0.0f, 0, r, any);
+            if (r[0] >= 1.0f) l2 = mid; else hi = mid;
         }
         tau = 0.5f * (l2 + hi);
     }
@@ -672,66 +715,74 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
             if (x > tau) { sx += x; kk += 1.0f; mn = fminf(mn, x); }
             else rest = fmaxf(rest, x);
         });
-        sx = wave_sum(sx);
-        kk = wave_sum(kk);
-        mn = -wave_max(-mn);
-        rest = wave_max(rest);
-        float tcf = NAN;
-        if (kk > 0.0f) {
-            if constexpr (MODE == kModeBeta1) {
-                tcf = (sx - 1.0f) / kk;
-            } else {
-                const float mean = sx / kk;
-                float v = 0.0f;
-                each_cand([&](float x, int) {
-                    if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
-                });
-                v = wave_sum(v);
-                if (v <= 1.0f) tcf = mean - sqrtf((1.0f - v) / kk);
-            }
+        float r[4];
+        bool any;
+        head_sums(wave_sum(sx), wave_sum(kk), -wave_max(-mn), wave_max(rest), 0, r, any);
+        // r[2], r[3] (sums) are unused: the min and the max are taken over the waves
+        float mnh = INFINITY, resth = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) {
+            mnh = fminf(mnh, part[pb][j * W + w2][2]);
+            resth = fmaxf(resth, part[pb][j * W + w2][3]);
         }
-        if (tcf == tcf && mn > tcf && !(rest > tcf)) tau = tcf;
+        const float sxh = r[0], kkh = r[1];
+        float tcf = NAN;
+        if constexpr (MODE == kModeBeta1) {
+            if (kkh > 0.0f) tcf = (sxh - 1.0f) / kkh;
+        } else {
+            const float mean = kkh > 0.0f ? sxh / kkh : 0.0f;
+            float v = 0.0f;
+            each_cand([&](float x, int) {
+                if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
+            });
+            head_sums(wave_sum(v), 0.0f, 0.0f, 0.0f, 0, r, any);
+            if (kkh > 0.0f && r[0] <= 1.0f) tcf = mean - sqrtf((1.0f - r[0]) / kkh);
+        }
+        if (tcf == tcf && mnh > tcf && !(resth > tcf)) tau = tcf;
     }
 
     // 4. support size and dropped mass with respect to tau_ref
     int ns = 0;
     float kept = 0.0f;
     const float tref = tau_ref ? tau_ref[oh] : 0.0f;
-    each_cand([&](float x, int) {
+    if (!empty) each_cand([&](float x, int) {
         ns += x > tau ? 1 : 0;
         if (delta_out && x > tref) kept += pw<MODE>(x - tref, beta);
     });
     const int sinc = wave_incl_scan(ns);
-    const int nsup = __shfl(sinc, 63, 64);
-    if (delta_out) kept = wave_sum(kept);
-    if (lane == 0) {
-        tau_out[oh] = tau;
-        if (support_out) support_out[oh] = nsup;
-        if (delta_out) delta_out[oh] = 1.0f - kept;
+    const int nsw = __builtin_amdgcn_readlane(sinc, 63);      // this wave's support
+    {
+        float r[4];
+        bool any;
+        head_sums((float)nsw, delta_out ? wave_sum(kept) : 0.0f, 0.0f, 0.0f, 0, r, any);
+        if (w == 0 && lane == 0) {
+            tau_out[oh] = empty ? -INFINITY : tau;
+            if (support_out) support_out[oh] = empty ? 0 : (int32_t)r[0];
+            if (delta_out) delta_out[oh] = empty ? 1.0f : 1.0f - r[1];
+        }
     }
 
-    // 5. PV over the support, in passes of kPvList entries.
+    // 5. PV over this wave's part of the support, in passes of PW entries.
     const int rg = lane >> 4, l16 = lane & (kRow - 1);
-    int* ls = pv_slot[j];
-    float* lpv = pv_p[j];
-    const int* phl = phys_of[j];
+    int* ls = pv_slot[wv];
+    float* lpv = pv_p[wv];
     float acc[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
-    for (int start = 0; start < nsup; start += kPvList) {
+    for (int start = 0; start < nsw; start += PW) {
         if (start > 0) wave_lds_sync();          // the previous pass has read its list
         int pos = sinc - ns - start;
-        const int dump = kPvList + lane;
+        const int dump = PW + lane;
         each_cand([&](float x, int slot) {
             if (x > tau) {
-                const int at = (pos >= 0 && pos < kPvList) ? pos : dump;
+                const int at = (pos >= 0 && pos < PW) ? pos : dump;
                 ls[at] = slot;
                 lpv[at] = pw<MODE>(x - tau, beta);
                 ++pos;
             }
         });
         wave_lds_sync();
-        const int nent = min(nsup - start, kPvList);
+        const int nent = min(nsw - start, PW);
         for (int e0 = 0; e0 < nent; e0 += 4 * PVU) {
             Vec<T, CH> vv[PVU];
             float pp[PVU];
@@ -743,7 +794,7 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
                 pp[u] = 0.0f;
                 if (e < nent) {
                     const int slot = ls[e];
-                    const int phys = phl[slot >> 4];
+                    const int phys = phys_of[slot >> 4];
                     if (phys >= 0) {
                         okv[u] = true;
                         pp[u] = lpv[e];
@@ -758,7 +809,7 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
                     for (int c = 0; c < CH; ++c) acc[c] = fmaf(pp[u], vv[u].get(c), acc[c]);
         }
     }
-    // Fixed-order sum of the four 16-lane rows; lanes 0..15 write.
+    // Fixed-order sums: the four 16-lane rows of the wave, then the head's waves.
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         float v = acc[c];
@@ -768,8 +819,16 @@ __global__ __launch_bounds__(64 * R) void sparse_tau_pv_kernel(
     }
     if (lane < kRow) {
 #pragma unroll
-        for (int c = 0; c < CH; c += 4)
-            *reinterpret_cast<float4*>(o + l16 * CH + c) = make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+        for (int c = 0; c < CH; ++c) pvout[wv][l16 * CH + c] = acc[c];
+    }
+    __syncthreads();
+    if (w == 0) {
+        for (int c = lane; c < D; c += 64) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < W; ++w2) v += pvout[j * W + w2][c];
+            o[c] = v;
+        }
     }
 }
 
@@ -808,15 +867,20 @@ static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_c
                             float alpha, float beta, const float* logits, const float* tau_ref, float* out,
                             float* tau, int32_t* support, float* delta, hipStream_t s) {
     const int units = d.B * d.G;
-#define EKV_FUSED(KK)                                                                                      \
-    sparse_tau_pv_kernel<T, D, R, KK, MODE><<<dim3(units), dim3(64 * R), 0, s>>>(                          \
-        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
-        tau_ref, out, tau, support, delta);                                                                \
-    return hipGetLastError();
-    if (pl.nslot <= 256) { EKV_FUSED(1) }
-    if (pl.nslot <= 512) { EKV_FUSED(2) }
-    if (pl.nslot <= 1024) { EKV_FUSED(4) }
-    if (pl.nslot <= 2048) { EKV_FUSED(8) }
+    // KPL float4 of logits per lane in all; W = 16 / R waves per head, at most KPL.
+    constexpr int WMAX = 16 / R;
+#define EKV_FUSED(KPL)                                                                                      \
+    {                                                                                                       \
+        constexpr int W = WMAX < KPL ? WMAX : KPL;                                                          \
+        sparse_tau_pv_kernel<T, D, R, W, KPL / W, MODE><<<dim3(units), dim3(64 * R * W), 0, s>>>(           \
+            (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
+            tau_ref, out, tau, support, delta);                                                             \
+        return hipGetLastError();                                                                           \
+    }
+    if (pl.nslot <= 256) EKV_FUSED(1)
+    if (pl.nslot <= 512) EKV_FUSED(2)
+    if (pl.nslot <= 1024) EKV_FUSED(4)
+    if (pl.nslot <= 2048) EKV_FUSED(8)
     EKV_FUSED(16)
 #undef EKV_FUSED
 }

@@ -203,16 +203,49 @@ __device__ __forceinline__ void block_sum3(float& a, float& b, float& c, float* 
     c = sc;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele on
-// shuffles; integer, so the order does not matter).
+// Integer DPP move: lanes whose source is outside the row read 0 when BC.
+template <int CTRL, int ROWMASK = 0xf, bool BC = true>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xf, BC);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in registers:
+// Hillis-Steele within each 16-lane row (row_shr 1, 2, 4, 8), then lane 15
+// of rows 0 and 2 is added into rows 1 and 3 (row_bcast:15), and lane 31
+// into rows 2 and 3 (row_bcast:31).  Integer, so exact.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
+    v += dpp_i<0x111>(v);
+    v += dpp_i<0x112>(v);
+    v += dpp_i<0x114>(v);
+    v += dpp_i<0x118>(v);
+    v += dpp_i<0x142, 0xa, false>(v);
+    v += dpp_i<0x143, 0xc, false>(v);
     return v;
+}
+
+// Wave-uniform integer sum (exact).
+__device__ __forceinline__ int wave_isum(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+
+// Wave-uniform unsigned min / max (row rotations, then the four rows).
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+    v = min(v, (uint32_t)dpp_i<0x128, 0xf, false>((int)v));
+    v = min(v, (uint32_t)dpp_i<0x124, 0xf, false>((int)v));
+    v = min(v, (uint32_t)dpp_i<0x122, 0xf, false>((int)v));
+    v = min(v, (uint32_t)dpp_i<0x121, 0xf, false>((int)v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<0x128, 0xf, false>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x124, 0xf, false>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x122, 0xf, false>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x121, 0xf, false>((int)v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
 }
 
 // Block-wide exclusive prefix sums of two per-thread counts, in thread
@@ -249,12 +282,9 @@ __device__ __forceinline__ void block_excl_scan2(int a, int b, int& ea, int& eb,
 // LDS of at least 3*NW ints.  Ends with a barrier.
 template <int NW>
 __device__ __forceinline__ void block_count_range(int c, uint32_t& mn, uint32_t& mx, int* total, int* wsum) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        c += __shfl_xor(c, off, 64);
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    }
+    c = wave_isum(c);
+    mn = wave_umin(mn);
+    mx = wave_umax(mx);
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         wsum[wid] = c;

@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 const size_t o = ((size_t)b * HQ + g * R + j) * MP + p;
                 const float dm = mu[o] - theta[j];
                 const float sg = sigma[o];
-                const float t = sg > 0.0f ? dm / sg : (dm > 0.0f ? INFINITY : -INFINITY);
+                const float t = sg > 0.0f ? dm * __builtin_amdgcn_rcpf(sg) : (dm > 0.0f ? INFINITY : -INFINITY);
                 f = fmaxf(f, t);
             }
         } else {
@@ -392,12 +392,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     c4[i] = hist[255 - 4 * l - i];
                     sum += c4[i];
                 }
-                int incl = sum;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int o = __shfl_up(incl, off, 64);
-                    if (l >= off) incl += o;
-                }
+                const int incl = wave_incl_scan(sum);
                 const uint64_t hit = __ballot(incl >= remaining);
                 const int L = hit ? (int)__builtin_ctzll(hit) : 63;
                 if (l == L) {
@@ -498,7 +493,8 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
                     const float dm = m[i] - theta;
-                    const float t = sg[i] > 0.0f ? dm / sg[i] : (dm > 0.0f ? INFINITY : -INFINITY);
+                    const float t = sg[i] > 0.0f ? dm * __builtin_amdgcn_rcpf(sg[i])
+                                                 : (dm > 0.0f ? INFINITY : -INFINITY);
                     f[i] = fmaxf(f[i], t);
                 }
             }
