@@ -33,6 +33,7 @@ namespace ekv {
 
 enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
 constexpr int kLogitUnroll = 4;
+constexpr int kMaxLogitPpb = 32;       // pages per logits block at most (plan_decode: 8 or 32)
 constexpr int kCandCap = 8192;
 
 // -------------------------------------------------------------- logits ----
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(256) void logits_kernel(
     constexpr int NW = Vec<T, CH>::NW;
     extern __shared__ float stage[];           // [R][ppb * kPage] logits of this chunk
     __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
+    __shared__ int sh_lp[kMaxLogitPpb], sh_phys[kMaxLogitPpb];
     const int ppb = 1 << lg_ppb;
     const int unit = blockIdx.y;
     const int b = unit / G, g = unit - b * G;
@@ -68,6 +70,18 @@ __global__ __launch_bounds__(256) void logits_kernel(
     float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
     const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
 
+    // The chunk's pages: logical index and physical tile, resolved once (one
+    // selection -> page-table chain per block instead of one per page and row).
+    for (int t = threadIdx.x; t < ppb; t += blockDim.x) {
+        const int ii = i0 + t;
+        const int lp = ii < i1 ? (sel ? sel[ii] : ii) : -1;
+        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
+        const bool ok = phys >= 0 && phys < NP;
+        sh_lp[t] = ok ? lp : -1;
+        sh_phys[t] = ok ? phys : -1;
+    }
+    __syncthreads();
+
     for (int i = i0; i < i1; i += kLogitUnroll) {
         Vec<T, CH> kv[kLogitUnroll];
         int lp[kLogitUnroll];
@@ -75,10 +89,9 @@ __global__ __launch_bounds__(256) void logits_kernel(
 #pragma unroll
         for (int u = 0; u < kLogitUnroll; ++u) {
             const int ii = i + u;
-            lp[u] = ii < i1 ? (sel ? sel[ii] : ii) : -1;
-            ok[u] = lp[u] >= 0 && lp[u] < M;
-            int phys = ok[u] ? page_table[(size_t)b * MP + lp[u]] : -1;
-            ok[u] = ok[u] && phys >= 0 && phys < NP;
+            lp[u] = ii < i1 ? sh_lp[ii - i0] : -1;
+            const int phys = ii < i1 ? sh_phys[ii - i0] : -1;
+            ok[u] = lp[u] >= 0;
             if (ok[u]) kv[u].load(k_cache + (((size_t)phys * G + g) * kPage + row) * D + lane * CH);
         }
 #pragma unroll
