@@ -36,7 +36,13 @@ constexpr int kTauMaxIter = 40;
 constexpr float kTauTol = 1e-5f;       // stop once a step is below this (relative)
 constexpr int kTauSub = 16;            // warm start: every 16th page ...
 constexpr int kTauSubMin = 2048;       // ... for sequences of at least this many pages
-constexpr float kTauSubTol = 1e-4f;
+constexpr float kTauSubTol = 1e-3f;     // below the subsample's own error (about 1e-2)
+// Early stop of the passes over all pages (see gauss_tau_solve).  Measured on
+// the clustered 128K workload (fp64 replay of the iteration): from the
+// warm start (relative error ~1e-2) one Halley step leaves ~1e-7 and one
+// Newton step ~4e-5.
+constexpr float kTauAcceptHalley = 3e-2f;
+constexpr float kTauAcceptNewton = 1e-3f;
 
 // Standard normal upper tail Q(x) = 1 - Phi(x), x >= 0, as phi(x) R(x) with
 // the Mills ratio R(x) ~ t h(t), t = 1/(1 + kMillsK x), h the polynomial
@@ -130,12 +136,17 @@ __device__ __forceinline__ void gauss_sums(const float2* __restrict__ src, const
 // times the Newton step on F^(1/beta), which is convex (an L^beta norm of
 // (Y - tau)_+ over the page mixture) and so never passes the root.  A step
 // that leaves the bracket is replaced by its midpoint.
+// The iteration stops after a step below `tol` (relative), or after an
+// unmodified Halley / Newton step below `accept`: the error left after such a
+// step is of order C step^3 (Halley) or C step^2 (Newton), far below `tol`
+// for the `accept` values used (kTauAcceptHalley, kTauAcceptNewton), so the
+// confirming pass over all pages is skipped.
 // WAVE: one wave runs the whole iteration with wave-level sums and no block
 // barrier; otherwise the block shares the pages and sums across waves.
 template <int BETA, bool WAVE, bool STAGED>
 __device__ float gauss_tau_solve(const float2* __restrict__ src, const float* __restrict__ mrow,
                                  const float* __restrict__ srow, int count, int last, float w, float w_last,
-                                 float a, float lo, float t, float tol, float* red, int& phase) {
+                                 float a, float lo, float t, float tol, float accept, float* red, int& phase) {
     constexpr float fb = (float)BETA;
     float hi = INFINITY;
     const int first = WAVE ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
@@ -153,18 +164,27 @@ __device__ float gauss_tau_solve(const float2* __restrict__ src, const float* __
         if (f >= 1.0f) lo = fmaxf(lo, t); else hi = fminf(hi, t);
         if (f == 1.0f) break;
         float step_t = NAN;
+        bool pure = false;                                      // an unmodified Halley / Newton step
         if (d1 > 0.0f && f > 0.0f) {
             const float L = logf(f);
             const float dL = -fb * d1 / f;                      // d log F / d tau
             step_t = -L / dL;
+            pure = BETA == 1;
             if constexpr (BETA >= 2) {
                 const float d2L = fb * (fb - 1.0f) * d2 / f - dL * dL;
                 const float den = 2.0f * dL * dL - L * d2L;
-                if (den > 0.0f) step_t = -2.0f * L * dL / den;
+                if (den > 0.0f) {
+                    step_t = -2.0f * L * dL / den;
+                    pure = true;
+                }
             }
             if (f > 1.0f) {
                 const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
-                step_t = fminf(step_t, 4.0f * (1.0f - 1.0f / gr) * f / d1);
+                const float cap = 4.0f * (1.0f - 1.0f / gr) * f / d1;
+                if (cap < step_t) {
+                    step_t = cap;
+                    pure = false;
+                }
             }
         }
         float nt = t + step_t;
@@ -172,8 +192,10 @@ __device__ float gauss_tau_solve(const float2* __restrict__ src, const float* __
             if (!(hi < INFINITY) || !(lo > -INFINITY)) break;   // no usable step, no finite bracket
             nt = 0.5f * (lo + hi);
             step_t = nt - t;
+            pure = false;
         }
-        const bool done = fabsf(step_t) <= tol * fmaxf(1.0f, fabsf(t));
+        const float scale = fmaxf(1.0f, fabsf(t));
+        const bool done = fabsf(step_t) <= tol * scale || (pure && fabsf(step_t) <= accept * scale);
         t = nt;
         if (done) break;
     }
@@ -250,18 +272,19 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
         __shared__ float sh_t;
         if (threadIdx.x < 64) {                      // wave 0 alone; the others wait at the barrier
             const float ts = gauss_tau_solve<BETA, true, true>(sub2, mrow, srow, msub, -1, wsub, wsub, a,
-                                                               -INFINITY, lo, kTauSubTol, red, phase);
+                                                               -INFINITY, lo, kTauSubTol, 0.0f, red, phase);
             if (threadIdx.x == 0) sh_t = ts;
         }
         __syncthreads();
         t = sh_t;
     }
+    const float accept = BETA == 1 ? kTauAcceptNewton : kTauAcceptHalley;
     if (staged)
         t = gauss_tau_solve<BETA, false, true>(lds2, mrow, srow, M, M - 1, (float)kPage, last_np, a, lo, t,
-                                               kTauTol, red, phase);
+                                               kTauTol, accept, red, phase);
     else
         t = gauss_tau_solve<BETA, false, false>(lds2, mrow, srow, M, M - 1, (float)kPage, last_np, a, lo, t,
-                                                kTauTol, red, phase);
+                                                kTauTol, accept, red, phase);
     if (threadIdx.x == 0) *out = t;
 }
 
