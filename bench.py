@@ -285,6 +285,7 @@ def main():
                                 "speedup_sparse_over_full": round(full_ms / ms_per_step, 3)}
         result["quality"] = {"coverage": round(cov, 5), "delta_mean": float(delta.mean()),
                              "delta_max": float(delta.max()), "R_mean": float(rel.mean()), "R_max": float(rel.max())}
+        full_tau = full.tau.clone()
         del full
         soft = ekv.FullDecoder(wl, 1.0)
         soft_ms = time_full(soft.run)
@@ -296,33 +297,45 @@ def main():
 
     if not args.no_variants and selector == "gauss" and args.stat_dtype == "f32":
         # Same step with the page mean/variance stored in bf16 (half the
-        # statistics bytes); reported beside the fp32 headline, not as it.
-        dec16 = ekv.Decoder(wl, selector, alpha, budget, z=z, stat_dtype="bf16")
-        dec16.build_stats()
-        for _ in range(max(args.warmup // 2, 3)):
-            dec16.step()
-        torch.cuda.synchronize()
-        ev16 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                 torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for a, b2, c2 in ev16:
-            a.record(stream)
-            dec16.score()
-            b2.record(stream)
-            dec16.select()
-            dec16.decode()
-            c2.record(stream)
-        torch.cuda.synchronize()
-        wall16 = time.perf_counter() - t0
-        sk16 = statistics.mean([a.elapsed_time(b2) for a, b2, _ in ev16]) * 1e3
-        b16 = score_kernel_bytes(wl, selector, 2)
-        result["variants"] = {"bf16_page_mean_var": {
-            "value": round(args.steps / wall16, 3), "unit": "steps/s",
-            "ms_per_step": round(wall16 * 1e3 / args.steps, 4),
-            "score_kernel_us": round(sk16, 2), "score_kernel_gbps": round(b16 / (sk16 * 1e-6) / 1e9, 1),
-            "note": "page mean/variance stored as bf16 (fp32 accumulation); min/max unaffected"}}
-        del dec16
-        torch.cuda.synchronize()
+        # statistics bytes) and in FP8 E4M3 (a quarter); reported beside the
+        # fp32 headline, not as it.
+        result["variants"] = {}
+        for sd, nbytes, note in (("bf16", 2, "page mean/variance stored as bf16 (fp32 accumulation); min/max unaffected"),
+                                 ("fp8", 1, "page mean/variance stored as OCP FP8 E4M3 (round to nearest even, "
+                                            "saturating at 448); min/max unaffected")):
+            dv = ekv.Decoder(wl, selector, alpha, budget, z=z, stat_dtype=sd)
+            dv.build_stats()
+            for _ in range(max(args.warmup // 2, 3)):
+                dv.step()
+            torch.cuda.synchronize()
+            evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+            t0 = time.perf_counter()
+            for a, b2, c2 in evv:
+                a.record(stream)
+                dv.score()
+                b2.record(stream)
+                dv.select()
+                dv.decode()
+                c2.record(stream)
+            torch.cuda.synchronize()
+            wallv = time.perf_counter() - t0
+            skv = statistics.mean([a.elapsed_time(b2) for a, b2, _ in evv]) * 1e3
+            bv = score_kernel_bytes(wl, selector, nbytes)
+            entry = {"value": round(args.steps / wallv, 3), "unit": "steps/s",
+                     "ms_per_step": round(wallv * 1e3 / args.steps, 4),
+                     "score_kernel_us": round(skv, 2), "score_kernel_gbps": round(bv / (skv * 1e-6) / 1e9, 1),
+                     "note": note}
+            if not args.no_full:
+                dlt = torch.empty_like(dv.buf.tau)
+                dv.decode(tau_ref=full_tau, delta=dlt)
+                torch.cuda.synchronize()
+                entry["quality"] = {"coverage": round(float(dv.buf.sel_count.sum().item()) * cfg.page_size /
+                                                      (cfg.num_kv_groups * sum(wl.seq_lens_host)), 5),
+                                    "delta_mean": float(dlt.mean()), "delta_max": float(dlt.max())}
+            result["variants"][f"{sd}_page_mean_var"] = entry
+            del dv
+            torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         rnd = None

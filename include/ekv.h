@@ -70,7 +70,11 @@ typedef enum {
     EKV_ERR_HIP = 4            /* a HIP launch or runtime call failed        */
 } ekv_status;
 
-typedef enum { EKV_F32 = 0, EKV_BF16 = 1 } ekv_dtype;
+/* EKV_FP8_E4M3 (statistics storage only): OCP FP8 E4M3 -- 1 sign, 4 exponent
+ * bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 = NaN, largest
+ * finite 448.  Written by rounding the fp32 statistic to nearest even;
+ * finite magnitudes beyond 448 saturate to 448. */
+typedef enum { EKV_F32 = 0, EKV_BF16 = 1, EKV_FP8_E4M3 = 2 } ekv_dtype;
 
 typedef enum {
     EKV_SEL_TOPK = 0,     /* [EKV] section 4.3 "Top-k page selection"            */
@@ -79,7 +83,8 @@ typedef enum {
 } ekv_selector;
 
 /* Problem shape.  Supported: D in {64, 128}; P == 16; r in {1, 2, 4, 8};
- * G <= 16; kv_dtype in {EKV_F32, EKV_BF16}; stat_dtype in {EKV_F32, EKV_BF16}. */
+ * G <= 16; kv_dtype in {EKV_F32, EKV_BF16}; stat_dtype in {EKV_F32, EKV_BF16,
+ * EKV_FP8_E4M3}. */
 typedef struct {
     int32_t batch;
     int32_t num_q_heads;
@@ -88,7 +93,7 @@ typedef struct {
     int32_t page_size;
     int32_t max_pages_per_seq;
     int32_t num_phys_pages;
-    int32_t kv_dtype;     /* ekv_dtype of q, k_cache, v_cache, kmin, kmax */
+    int32_t kv_dtype;     /* ekv_dtype of q, k_cache, v_cache, kmin, kmax (F32/BF16) */
     int32_t stat_dtype;   /* ekv_dtype of kmean, kvar                      */
 } ekv_shape;
 

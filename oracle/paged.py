@@ -62,6 +62,29 @@ def page_stats(K: np.ndarray, page_size: int):
     return kmin, kmax, mean, var
 
 
+def round_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest value of the 8-bit float format E4M3 of the OCP 8-bit floating
+    point specification (1 sign bit; 4 exponent bits, bias 7; 3 mantissa bits;
+    subnormal step 2^-9 below 2^-6; no infinities; largest finite 448), ties
+    to the even mantissa.  Finite magnitudes beyond 448 become 448 (the
+    storage reading for page mean/variance kept in this format, an option in
+    the spirit of R4); NaN stays NaN.
+
+    Written from the format definition: within the binade [2^e, 2^(e+1)),
+    e >= -6, the representable values are multiples of 2^(e-3); below 2^-6
+    they are multiples of 2^-9.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)
+    with np.errstate(invalid="ignore"):
+        v = np.minimum(np.round(a / step) * step, 448.0)   # np.round: half to even
+    return np.where(np.isnan(x), np.nan, np.copysign(v, x))
+
+
 def page_valid_counts(n: int, page_size: int) -> np.ndarray:
     """n_p for every logical page of a sequence of n tokens."""
     M = num_pages(n, page_size)

@@ -49,7 +49,7 @@ ekv_status check_shape(const ekv_shape* s, ekv::Dims* d) {
     if (s->page_size != 16) return fail(EKV_ERR_UNSUPPORTED, "page_size=%d (only 16 is built)", s->page_size);
     if (s->kv_dtype != EKV_F32 && s->kv_dtype != EKV_BF16)
         return fail(EKV_ERR_UNSUPPORTED, "kv_dtype=%d", s->kv_dtype);
-    if (s->stat_dtype != EKV_F32 && s->stat_dtype != EKV_BF16)
+    if (s->stat_dtype != EKV_F32 && s->stat_dtype != EKV_BF16 && s->stat_dtype != EKV_FP8_E4M3)
         return fail(EKV_ERR_UNSUPPORTED, "stat_dtype=%d", s->stat_dtype);
     if ((long long)s->max_pages_per_seq * 16 > 0x7fffffffLL)
         return fail(EKV_ERR_UNSUPPORTED, "max_pages_per_seq=%d too large", s->max_pages_per_seq);
@@ -63,7 +63,7 @@ ekv_status check_shape(const ekv_shape* s, ekv::Dims* d) {
     d->MP = s->max_pages_per_seq;
     d->NP = s->num_phys_pages;
     d->kv_bf16 = s->kv_dtype == EKV_BF16;
-    d->stat_bf16 = s->stat_dtype == EKV_BF16;
+    d->stat = s->stat_dtype == EKV_BF16 ? ekv::kStatBF16 : (s->stat_dtype == EKV_FP8_E4M3 ? ekv::kStatFP8 : ekv::kStatF32);
     return EKV_OK;
 }
 

@@ -20,6 +20,7 @@ namespace ekv {
 
 typedef uint16_t bf16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef uint8_t fp8_t;        // OCP FP8 E4M3 code (statistics storage only)
 
 constexpr int kPage = 16;     // tokens per page (the only page size built)
 constexpr int kRow = 16;      // lanes per DPP row
@@ -29,11 +30,13 @@ constexpr int kRow = 16;      // lanes per DPP row
 template <typename T, int CH>
 struct Vec {
     static constexpr int NW = CH * (int)sizeof(T) / 4;
-    static_assert(NW == 2 || NW == 4 || NW == 8, "row slice must be 8, 16 or 32 bytes");
+    static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "row slice must be 4, 8, 16 or 32 bytes");
     uint32_t w[NW];
 
     __device__ __forceinline__ void load(const T* p) {
-        if constexpr (NW == 2) {
+        if constexpr (NW == 1) {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        } else if constexpr (NW == 2) {
             uint2 a = *reinterpret_cast<const uint2*>(p);
             w[0] = a.x; w[1] = a.y;
         } else if constexpr (NW == 4) {
@@ -47,7 +50,9 @@ struct Vec {
         }
     }
     __device__ __forceinline__ void store(T* p) const {
-        if constexpr (NW == 2) {
+        if constexpr (NW == 1) {
+            *reinterpret_cast<uint32_t*>(p) = w[0];
+        } else if constexpr (NW == 2) {
             *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
         } else if constexpr (NW == 4) {
             *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -57,10 +62,17 @@ struct Vec {
             p4[1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
     }
-    // Channel i widened to fp32 (exact).
+    // Channel i widened to fp32 (exact).  FP8 codes go through the packed
+    // hardware conversion (checked against the E4M3 definition on all 256
+    // codes on gfx950).
     __device__ __forceinline__ float get(int i) const {
         if constexpr (std::is_same<T, float>::value) {
             return __uint_as_float(w[i]);
+        } else if constexpr (std::is_same<T, fp8_t>::value) {
+            const int word = (int)w[i >> 2];
+            const auto pair = ((i >> 1) & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
+                                             : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+            return pair[i & 1];
         } else {
             return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u)
                            : __uint_as_float(w[i >> 1] << 16);
@@ -77,6 +89,22 @@ struct Vec {
         }
     }
 };
+
+// fp32 -> OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; no infinities; S.1111.111 is NaN): round to nearest even, finite
+// magnitudes beyond the largest finite value 448 saturate to 448, NaN stays
+// NaN.  Below 2^-6 the grid is the subnormal step 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float f) {
+    const uint32_t s = (__float_as_uint(f) >> 24) & 0x80u;
+    const float a = fabsf(f);
+    if (!(a == a)) return s | 0x7fu;
+    if (a >= 448.0f) return s | 0x7eu;
+    if (a < 0.015625f) return s | (uint32_t)rintf(a * 512.0f);   // 0..8; 8 is the smallest normal
+    uint32_t u = __float_as_uint(a);
+    u += 0x7ffffu + ((u >> 20) & 1u);                             // round the 23-bit mantissa to 3 bits
+    const uint32_t e = (u >> 23) - 120u;                          // biased 7 instead of 127
+    return s | (e << 3) | ((u >> 20) & 7u);
+}
 
 // fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {

@@ -9,10 +9,12 @@
 
 namespace ekv {
 
+enum { kStatF32 = 0, kStatBF16 = 1, kStatFP8 = 2 };
+
 struct Dims {
     int B, HQ, G, R, D, MP, NP;
     int kv_bf16;     // 1 = bf16 KV, 0 = fp32
-    int stat_bf16;   // 1 = bf16 mean/var, 0 = fp32
+    int stat;        // mean/var storage: kStatF32, kStatBF16, kStatFP8
 };
 
 // Page statistics.

@@ -243,7 +243,7 @@ static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const
 template <typename T, typename S, int D, int R>
 static hipError_t run_gauss(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                             const void* kmean, const void* kvar, float* mu, float* sigma, hipStream_t s) {
-    int lg = score_lg_ppb(d, 2 * d.HQ, d.stat_bf16 ? 4 : 8);
+    int lg = score_lg_ppb(d, 2 * d.HQ, d.stat == kStatF32 ? 8 : 4);
     if (((size_t)2 * d.HQ << lg) * sizeof(float) > 48 * 1024 && !allow_64k_lds(gauss_score_kernel<T, S, D, R>))
         lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
@@ -280,14 +280,18 @@ hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_
                               float* mu, float* sigma, hipStream_t s) {
 #define EKV_GS(RR, T, S, DD) return run_gauss<T, S, DD, RR>(d, q, page_table, seq_lens, kmean, kvar, mu, sigma, s)
     if (d.kv_bf16) {
-        if (d.stat_bf16) {
+        if (d.stat == kStatBF16) {
             if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 64) }
+        } else if (d.stat == kStatFP8) {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, fp8_t, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, fp8_t, 64) }
         } else {
             if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, float, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, float, 64) }
         }
     } else {
-        if (d.stat_bf16) {
+        if (d.stat == kStatBF16) {
             if (d.D == 128) { EKV_R_SWITCH(EKV_GS, float, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GS, float, bf16_t, 64) }
+        } else if (d.stat == kStatFP8) {
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, float, fp8_t, 128) } else { EKV_R_SWITCH(EKV_GS, float, fp8_t, 64) }
         } else {
             if (d.D == 128) { EKV_R_SWITCH(EKV_GS, float, float, 128) } else { EKV_R_SWITCH(EKV_GS, float, float, 64) }
         }

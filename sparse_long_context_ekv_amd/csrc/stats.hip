@@ -21,7 +21,8 @@ namespace ekv {
 // lane's CH channels of token t, tokens 0..np-1 valid.  Writes this lane's
 // slice of kmin/kmax (exact selections of stored values, KV dtype) and
 // kmean/kvar (fp32 sum in token order / n_p; population variance by a second
-// pass over the registers; rounded to the statistics dtype) at `out`.
+// pass over the registers; rounded to the statistics dtype: fp32, bf16 or
+// FP8 E4M3, each round to nearest even, FP8 saturating at 448) at `out`.
 // Shared by the whole-cache build and the append path, so the two agree bit
 // for bit.
 template <typename T, int CH, typename S>
@@ -81,15 +82,30 @@ __device__ __forceinline__ void tile_stats_store(const Vec<T, CH> (&v)[kPage], i
                 *reinterpret_cast<float4*>(kvar + out + c) =
                     make_float4(var[c] / (float)np, var[c + 1] / (float)np, var[c + 2] / (float)np, var[c + 3] / (float)np);
             }
-        } else {
+        } else if constexpr (std::is_same<S, bf16_t>::value) {
             Vec<bf16_t, CH> a, c2;
 #pragma unroll
             for (int c = 0; c < CH; c += 2) {
                 a.w[c >> 1] = f32_to_bf16_rne(mean[c]) | (f32_to_bf16_rne(mean[c + 1]) << 16);
                 c2.w[c >> 1] = f32_to_bf16_rne(var[c] / (float)np) | (f32_to_bf16_rne(var[c + 1] / (float)np) << 16);
             }
-            a.store(reinterpret_cast<bf16_t*>(kmean) + out);
-            c2.store(reinterpret_cast<bf16_t*>(kvar) + out);
+            a.store(kmean + out);
+            c2.store(kvar + out);
+        } else {
+            Vec<fp8_t, CH> a, c2;
+#pragma unroll
+            for (int c = 0; c < CH; c += 4) {
+                uint32_t wm = 0, wv = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    wm |= f32_to_e4m3_sat(mean[c + k]) << (8 * k);
+                    wv |= f32_to_e4m3_sat(var[c + k] / (float)np) << (8 * k);
+                }
+                a.w[c >> 2] = wm;
+                c2.w[c >> 2] = wv;
+            }
+            a.store(kmean + out);
+            c2.store(kvar + out);
         }
     }
 }
@@ -189,11 +205,11 @@ hipError_t launch_page_stats(const Dims& d, const void* k_cache, const int32_t* 
     if (n_items <= 0) return hipSuccess;
 #define EKV_STATS(T, DD, S) return run_stats<T, DD, S>(d, k_cache, page_table, seq_lens, page_list, n_items, kmin, kmax, kmean, kvar, s)
     if (d.kv_bf16) {
-        if (d.D == 128) { if (d.stat_bf16) EKV_STATS(bf16_t, 128, bf16_t); else EKV_STATS(bf16_t, 128, float); }
-        else            { if (d.stat_bf16) EKV_STATS(bf16_t, 64, bf16_t);  else EKV_STATS(bf16_t, 64, float); }
+        if (d.D == 128) { switch (d.stat) { case kStatBF16: EKV_STATS(bf16_t, 128, bf16_t); case kStatFP8: EKV_STATS(bf16_t, 128, fp8_t); default: EKV_STATS(bf16_t, 128, float); } }
+        else            { switch (d.stat) { case kStatBF16: EKV_STATS(bf16_t, 64, bf16_t); case kStatFP8: EKV_STATS(bf16_t, 64, fp8_t); default: EKV_STATS(bf16_t, 64, float); } }
     } else {
-        if (d.D == 128) { if (d.stat_bf16) EKV_STATS(float, 128, bf16_t); else EKV_STATS(float, 128, float); }
-        else            { if (d.stat_bf16) EKV_STATS(float, 64, bf16_t);  else EKV_STATS(float, 64, float); }
+        if (d.D == 128) { switch (d.stat) { case kStatBF16: EKV_STATS(float, 128, bf16_t); case kStatFP8: EKV_STATS(float, 128, fp8_t); default: EKV_STATS(float, 128, float); } }
+        else            { switch (d.stat) { case kStatBF16: EKV_STATS(float, 64, bf16_t); case kStatFP8: EKV_STATS(float, 64, fp8_t); default: EKV_STATS(float, 64, float); } }
     }
 #undef EKV_STATS
 }
@@ -216,11 +232,11 @@ hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new,
                             void* kmean, void* kvar, int32_t* new_lens, hipStream_t s) {
 #define EKV_APP(T, DD, S) return run_append<T, DD, S>(d, k_new, v_new, page_table, seq_lens, k_cache, v_cache, kmin, kmax, kmean, kvar, new_lens, s)
     if (d.kv_bf16) {
-        if (d.D == 128) { if (d.stat_bf16) EKV_APP(bf16_t, 128, bf16_t); else EKV_APP(bf16_t, 128, float); }
-        else            { if (d.stat_bf16) EKV_APP(bf16_t, 64, bf16_t);  else EKV_APP(bf16_t, 64, float); }
+        if (d.D == 128) { switch (d.stat) { case kStatBF16: EKV_APP(bf16_t, 128, bf16_t); case kStatFP8: EKV_APP(bf16_t, 128, fp8_t); default: EKV_APP(bf16_t, 128, float); } }
+        else            { switch (d.stat) { case kStatBF16: EKV_APP(bf16_t, 64, bf16_t); case kStatFP8: EKV_APP(bf16_t, 64, fp8_t); default: EKV_APP(bf16_t, 64, float); } }
     } else {
-        if (d.D == 128) { if (d.stat_bf16) EKV_APP(float, 128, bf16_t); else EKV_APP(float, 128, float); }
-        else            { if (d.stat_bf16) EKV_APP(float, 64, bf16_t);  else EKV_APP(float, 64, float); }
+        if (d.D == 128) { switch (d.stat) { case kStatBF16: EKV_APP(float, 128, bf16_t); case kStatFP8: EKV_APP(float, 128, fp8_t); default: EKV_APP(float, 128, float); } }
+        else            { switch (d.stat) { case kStatBF16: EKV_APP(float, 64, bf16_t); case kStatFP8: EKV_APP(float, 64, fp8_t); default: EKV_APP(float, 64, float); } }
     }
 #undef EKV_APP
 }

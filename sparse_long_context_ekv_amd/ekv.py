@@ -22,7 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libekv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 SEL_TOPK, SEL_GAUSS, SEL_SUPERSET = 0, 1, 2
 _STATUS = {0: "EKV_OK", 1: "EKV_ERR_INVALID_ARG", 2: "EKV_ERR_UNSUPPORTED", 3: "EKV_ERR_WORKSPACE", 4: "EKV_ERR_HIP"}
 SYMBOLS = ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
@@ -96,9 +96,13 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+# torch storage dtype of page mean/variance per statistics dtype name
+STAT_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+
 def make_shape(batch, num_q_heads, num_kv_groups, head_dim, max_pages_per_seq, num_phys_pages,
                kv_dtype="bf16", stat_dtype="f32", page_size=16) -> Shape:
-    dt = {"f32": F32, "bf16": BF16, F32: F32, BF16: BF16}
+    dt = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, F32: F32, BF16: BF16, FP8_E4M3: FP8_E4M3}
     return Shape(batch, num_q_heads, num_kv_groups, head_dim, page_size, max_pages_per_seq,
                  num_phys_pages, dt[kv_dtype], dt[stat_dtype])
 
@@ -200,7 +204,7 @@ class Decoder:
                                 c.kv_dtype, stat_dtype)
         B, H, G, D, MP, NP = c.batch, c.num_q_heads, c.num_kv_groups, c.head_dim, wl.max_pages, wl.num_phys
         kvdt = wl.k_cache.dtype
-        sdt = torch.float32 if stat_dtype == "f32" else torch.bfloat16
+        sdt = STAT_TORCH_DTYPE[stat_dtype]
         self.stats = {}
         if self.selector == SEL_TOPK:
             self.stats["kmin"] = torch.empty(NP, G, D, dtype=kvdt, device=dev)

@@ -22,11 +22,16 @@ P = 16
 def _stats_buffers(wl, stat):
     c = wl.cfg
     NP, G, D = wl.num_phys, c.num_kv_groups, c.head_dim
-    sdt = torch.float32 if stat == "f32" else torch.bfloat16
+    sdt = ekv.STAT_TORCH_DTYPE[stat]
     return dict(kmin=torch.full((NP, G, D), 7.0, dtype=wl.k_cache.dtype, device="cuda"),
                 kmax=torch.full((NP, G, D), 7.0, dtype=wl.k_cache.dtype, device="cuda"),
-                kmean=torch.full((NP, G, D), 7.0, dtype=sdt, device="cuda"),
-                kvar=torch.full((NP, G, D), 7.0, dtype=sdt, device="cuda"))
+                kmean=torch.full((NP, G, D), 7.0).to(sdt).to("cuda"),
+                kvar=torch.full((NP, G, D), 7.0).to(sdt).to("cuda"))
+
+
+def _bits(t):
+    """Storage bits of a tensor, for bit-for-bit comparison."""
+    return t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16) if t.element_size() == 2 else t
 
 
 def _grown_workload(base, extra, cfg):
@@ -38,7 +43,7 @@ def _grown_workload(base, extra, cfg):
     return wl
 
 
-@pytest.mark.parametrize("stat", ["f32", "bf16"])
+@pytest.mark.parametrize("stat", ["f32", "bf16", "fp8"])
 def test_append_matches_rebuild_and_oracle(stat):
     T = 20
     base = [5000, 2048, 0, 37]            # mid-page, page boundary, empty, short
@@ -71,8 +76,7 @@ def test_append_matches_rebuild_and_oracle(stat):
     for b in range(B):
         rows = H.phys_rows(wl, b)
         for key in st:                                          # bit for bit against a rebuild
-            assert torch.equal(st[key][rows].view(torch.int16) if st[key].dtype == torch.bfloat16 else st[key][rows],
-                               fresh[key][rows].view(torch.int16) if fresh[key].dtype == torch.bfloat16 else fresh[key][rows]), (b, key)
+            assert torch.equal(_bits(st[key])[rows], _bits(fresh[key])[rows]), (b, key)
         q, K, V, n = H.seq_logical(wl, b)
         np.testing.assert_array_equal(K[base[b]:], K_new[b])   # appended tokens stored exactly
         np.testing.assert_array_equal(V[base[b]:], V_new[b])

@@ -50,11 +50,11 @@ def _shape(wl, stat="f32"):
 def _stats(wl, stat="f32"):
     c = wl.cfg
     NP, G, D = wl.num_phys, c.num_kv_groups, c.head_dim
-    sdt = torch.float32 if stat == "f32" else torch.bfloat16
+    sdt = ekv.STAT_TORCH_DTYPE[stat]
     st = dict(kmin=torch.full((NP, G, D), 7.0, dtype=wl.k_cache.dtype, device="cuda"),
               kmax=torch.full((NP, G, D), 7.0, dtype=wl.k_cache.dtype, device="cuda"),
-              kmean=torch.full((NP, G, D), 7.0, dtype=sdt, device="cuda"),
-              kvar=torch.full((NP, G, D), 7.0, dtype=sdt, device="cuda"))
+              kmean=torch.full((NP, G, D), 7.0).to(sdt).to("cuda"),
+              kvar=torch.full((NP, G, D), 7.0).to(sdt).to("cuda"))
     ekv.build_page_stats(_shape(wl, stat), wl.k_cache, wl.page_table, wl.seq_lens, **st)
     return st
 
@@ -83,6 +83,26 @@ def test_page_stats_bf16_storage():
     for key in ("kmean", "kvar"):
         want = st32[key].to(torch.bfloat16)
         assert torch.equal(st16[key].view(torch.int16), want.view(torch.int16))
+
+
+def test_page_stats_fp8_storage():
+    """FP8 E4M3 mean/var are the fp32 statistics rounded to nearest even
+    (oracle.paged.round_fp8_e4m3 applied to the fp32 statistics), code for
+    code."""
+    wl = workload("gauss-ragged")
+    st32 = _stats(wl, "f32")
+    st8 = _stats(wl, "fp8")
+    H.sync()
+    for key in ("kmean", "kvar"):
+        want = oracle.paged.round_fp8_e4m3(H.to_np(st32[key]))
+        got = st8[key].cpu().to(torch.float64).numpy()          # exact up-cast, on the host
+        np.testing.assert_array_equal(got, want)
+
+
+def _stored_stats_logical(st, wl, b):
+    """The stored mean/var of sequence b, up-cast exactly, in logical page order."""
+    rows = H.phys_rows(wl, b)
+    return (st["kmean"].cpu().to(torch.float64).numpy()[rows], st["kvar"].cpu().to(torch.float64).numpy()[rows])
 
 
 def test_page_stats_page_list():
@@ -128,7 +148,7 @@ def test_box_scores(name):
         assert bool((score[b, :, M:] == -7.0).all())                   # past the end: untouched
 
 
-@pytest.mark.parametrize("stat", ["f32", "bf16"])
+@pytest.mark.parametrize("stat", ["f32", "bf16", "fp8"])
 def test_gauss_moments(stat):
     wl = workload("gauss-ragged")
     c = wl.cfg
@@ -146,9 +166,13 @@ def test_gauss_moments(stat):
         _, _, mean, var = oracle.paged.page_stats(K, P)
         if rnd:
             mean, var = rnd(mean), rnd(var)
+        if stat == "fp8":
+            # scoring checked on the stored 8-bit statistics themselves (the
+            # storage rounding has its own test above)
+            mean, var = _stored_stats_logical(st, wl, b)
         omu, osg = oracle.paged.gauss_moments(q, mean, var)
         M = omu.shape[1]
-        tol = 1e-5 if stat == "f32" else 2e-2
+        tol = 2e-2 if stat == "bf16" else 1e-5
         np.testing.assert_allclose(H.to_np(mu[b, :, :M]), omu, rtol=tol, atol=tol * np.abs(omu).max())
         np.testing.assert_allclose(H.to_np(sg[b, :, :M]), osg, rtol=tol, atol=tol * np.abs(osg).max())
 
@@ -204,6 +228,38 @@ def test_gauss_threshold_and_selection():
                 np.testing.assert_array_equal(got, want)
             else:
                 H.compare_selection(got, want, t, len(want), rel=1e-3)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_gauss_selection_fp8_statistics(alpha):
+    """The Gaussian selector on FP8 E4M3 page mean/variance: threshold and
+    page set against the oracle run on the same stored statistics."""
+    wl = workload("gauss-ragged")
+    c = wl.cfg
+    cap = 64
+    dec = ekv.Decoder(wl, "gauss", alpha, cap, z=c.z, stat_dtype="fp8")
+    dec.build_stats()
+    dec.score()
+    dec.select()
+    H.sync()
+    r = c.num_q_heads // c.num_kv_groups
+    for b in range(c.batch):
+        q = H.to_np(wl.q[b])
+        n = wl.seq_lens_host[b]
+        mean, var = _stored_stats_logical(dec.stats, wl, b)
+        mu, sg = oracle.paged.gauss_moments(q, mean, var)
+        n_p = oracle.paged.page_valid_counts(n, P)
+        th = np.array([oracle.select.gauss_tau_hat(mu[h], sg[h], n_p, alpha) for h in range(c.num_q_heads)])
+        got_th = H.to_np(dec.buf.tau_hat[b])
+        for h in range(c.num_q_heads):
+            assert H.tau_close(got_th[h], th[h]), (b, h, got_th[h], th[h])
+        for g in range(c.num_kv_groups):
+            hs = slice(g * r, (g + 1) * r)
+            t = oracle.select.gauss_margins(mu[hs], sg[hs], th[hs], alpha)
+            want = oracle.select.gauss_select(mu[hs], sg[hs], th[hs], alpha, c.z, cap)
+            cnt = int(dec.buf.sel_count[b, g])
+            got = dec.buf.sel_pages[b, g, :cnt].cpu().numpy()
+            H.compare_selection(got, want, t, len(want), rel=1e-3)
 
 
 def _oracle_sel_tensor(sels, B, G, budget):
