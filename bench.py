@@ -113,7 +113,14 @@ def cpu_baseline(wl, selector, alpha, budget, z, nseq, stat_round=None):
     P, G, H = c.page_size, c.num_kv_groups, c.num_q_heads
     r = H // G
     B = c.batch
-    picks = sorted(set([0, B - 1] + list(range(1, B - 1))[: max(0, nseq - 2)]))[:nseq]
+    lens = wl.seq_lens_host
+    if len(set(lens)) == 1:
+        picks = sorted(set([0, B - 1] + list(range(1, B - 1))[: max(0, nseq - 2)]))[:nseq]
+    else:
+        # ragged batch: sequences at evenly spaced length quantiles, longest included
+        order = sorted(range(B), key=lambda i: lens[i])
+        k = max(1, min(nseq, B))
+        picks = sorted({order[round((B - 1) * (j + 1) / k)] for j in range(k)})
     times = []
     for b in picks:
         q, kc, vc, pt, n = W.host_sequence(wl, b)
@@ -136,9 +143,12 @@ def cpu_baseline(wl, selector, alpha, budget, z, nseq, stat_round=None):
         times.append(time.perf_counter() - t0)
         log(f"oracle sequence {b}: {times[-1]:.2f} s")
     per_seq = statistics.mean(times)
-    return {"value": 1.0 / (per_seq * B), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(picks)} of {B} sequences (b={picks}), fp64 numpy/scipy oracle, same stages as the "
-                      f"GPU step (page statistics precomputed); per-sequence mean time x {B} sequences = one step",
+    # one step = the whole batch: the sample's time per token times the batch's tokens
+    step_s = sum(times) * sum(lens) / sum(lens[b] for b in picks)
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(picks)} of {B} sequences (b={picks}, {sum(lens[b] for b in picks)} of {sum(lens)} "
+                      f"tokens), fp64 numpy/scipy oracle, same stages as the GPU step (page statistics "
+                      f"precomputed); sample time scaled by the batch's token count = one step",
             "seconds_per_sequence": per_seq}
 
 
