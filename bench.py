@@ -286,15 +286,18 @@ def main():
         full = ekv.FullDecoder(wl, alpha)
         full_ms = time_full(full.run)
         delta = torch.empty_like(dec.buf.tau)
-        dec.decode(tau_ref=full.tau, delta=delta)
+        supref = torch.empty_like(dec.buf.support)
+        dec.decode(tau_ref=full.tau, delta=delta, support_ref=supref)
         torch.cuda.synchronize()
+        rho = (supref.double() / full.support.double().clamp(min=1.0)).flatten()
         P = cfg.page_size
         cov = float(dec.buf.sel_count.sum().item()) * P / (cfg.num_kv_groups * sum(wl.seq_lens_host))
         rel = ((dec.buf.out - full.out).norm(dim=2) / full.out.norm(dim=2)).flatten()
         result["full_cache"] = {"ms_per_step": round(full_ms, 4),
                                 "speedup_sparse_over_full": round(full_ms / ms_per_step, 3)}
         result["quality"] = {"coverage": round(cov, 5), "delta_mean": float(delta.mean()),
-                             "delta_max": float(delta.max()), "R_mean": float(rel.mean()), "R_max": float(rel.max())}
+                             "delta_max": float(delta.max()), "rho_mean": float(rho.mean()),
+                             "rho_min": float(rho.min()), "R_mean": float(rel.mean()), "R_max": float(rel.max())}
         full_tau = full.tau.clone()
         del full
         soft = ekv.FullDecoder(wl, 1.0)

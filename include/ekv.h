@@ -204,9 +204,13 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  *   alpha == 1); support [B][HQ] int32 nonzero count (NULL ok);
  *   delta [B][HQ] fp32 (NULL ok; needs tau_ref): dropped mass
  *   1 - sum_{j in C_tok} p_ref_j of the distribution whose threshold is
- *   tau_ref [B][HQ] (e.g. a full-cache decode's tau) ([EKV] section 3.1).
+ *   tau_ref [B][HQ] (e.g. a full-cache decode's tau) ([EKV] section 3.1);
+ *   support_ref [B][HQ] int32 (NULL ok; needs tau_ref): the number of tokens
+ *   of C_tok with p_ref > 0 (x_j > tau_ref; every token for alpha == 1).
+ *   Divided by the full-cache decode's support it is the support recall rho
+ *   of [EKV] section 3.1 and Appendix E.1.
  * An empty candidate set (seq_lens[b] == 0 or sel_count == 0) gives
- *   out = 0, tau = -inf, support = 0, delta = 1.
+ *   out = 0, tau = -inf, support = 0, delta = 1, support_ref = 0.
  * Needs a workspace (see conventions); its size depends on sel_pages being
  * NULL or not and on sel_stride.                                           */
 ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
@@ -215,6 +219,7 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
                              const int32_t* sel_pages, const int32_t* sel_count,
                              int32_t sel_stride, float alpha, const float* tau_ref,
                              float* out, float* tau, int32_t* support, float* delta,
+                             int32_t* support_ref,
                              void* workspace, size_t* workspace_bytes, void* stream);
 
 /* Message describing the last error returned on this thread ("" if none). */

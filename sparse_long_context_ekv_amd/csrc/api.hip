@@ -77,7 +77,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 extern "C" {
 
-int32_t ekv_abi_version(void) { return 2; }
+int32_t ekv_abi_version(void) { return 3; }
 
 const char* ekv_last_error(void) { return g_err; }
 
@@ -186,7 +186,8 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
 ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens, const int32_t* sel_pages,
                              const int32_t* sel_count, int32_t sel_stride, float alpha, const float* tau_ref,
-                             float* out, float* tau, int32_t* support, float* delta, void* workspace,
+                             float* out, float* tau, int32_t* support, float* delta, int32_t* support_ref,
+                             void* workspace,
                              size_t* workspace_bytes, void* stream) {
     ekv::Dims d;
     ekv_status st = check_shape(shape, &d);
@@ -197,6 +198,7 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
     if (sparse && sel_stride < 1) return fail(EKV_ERR_INVALID_ARG, "sel_stride=%d < 1", sel_stride);
     if (sparse && !sel_count) return fail(EKV_ERR_INVALID_ARG, "sel_count is required with sel_pages");
     if (delta && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "delta needs tau_ref");
+    if (support_ref && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "support_ref needs tau_ref");
     const ekv::DecodePlan pl = ekv::plan_decode(d, sparse, sparse ? sel_stride : 0, alpha);
     if (!workspace) {
         *workspace_bytes = pl.bytes;
@@ -208,7 +210,7 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
     if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !tau)
         return fail(EKV_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, seq_lens, out and tau are required");
     return hip_status(ekv::launch_decode(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count,
-                                         sel_stride, alpha, tau_ref, out, tau, support, delta, (char*)workspace,
+                                         sel_stride, alpha, tau_ref, out, tau, support, delta, support_ref, (char*)workspace,
                                          (hipStream_t)stream),
                       "ekv_entmax_decode");
 }

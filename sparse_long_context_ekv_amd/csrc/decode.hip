@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void tau_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
     int mode, float alpha, float beta, const float* __restrict__ tau_ref, float* __restrict__ tau_out,
-    int32_t* __restrict__ support_out, float* __restrict__ delta_out) {
+    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
     __shared__ float cand[kCandCap];
     __shared__ float red[8];
     __shared__ int wsum[4];
@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256) void tau_kernel(
             tau_out[oh] = -INFINITY;
             if (support_out) support_out[oh] = 0;
             if (delta_out) delta_out[oh] = 1.0f;
+            if (supref_out) supref_out[oh] = 0;
         }
         return;
     }
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(256) void tau_kernel(
             tau_out[oh] = lse;
             if (support_out) support_out[oh] = (int32_t)C;
             if (delta_out) delta_out[oh] = 1.0f - kept;
+            if (supref_out) supref_out[oh] = (int32_t)C;      // softmax: every token has p > 0
         }
         return;
     }
@@ -331,12 +333,13 @@ __global__ __launch_bounds__(256) void tau_kernel(
 
     // Support size and dropped mass with respect to tau_ref.
     const TauSums fin = sums(tau, lo, false);
-    float kept = 0.0f;
-    if (delta_out) kept = sums(tref, lo, false).s1;
+    TauSums ref = {0.0f, 0.0f, 0.0f};
+    if (delta_out || supref_out) ref = sums(tref, lo, false);     // tref >= tau >= lo
     if (threadIdx.x == 0) {
         tau_out[oh] = tau;
         if (support_out) support_out[oh] = (int32_t)fin.k;
-        if (delta_out) delta_out[oh] = 1.0f - kept;
+        if (delta_out) delta_out[oh] = 1.0f - ref.s1;
+        if (supref_out) supref_out[oh] = (int32_t)ref.k;
     }
 }
 
@@ -522,7 +525,7 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
     int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
     float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
-    float* __restrict__ delta_out) {
+    float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
     constexpr int NWV = R * W;                   // waves in the block
     constexpr int CH = D / kRow;
     constexpr int PVU = 4;                       // V rows per 16-lane row in flight
@@ -755,23 +758,30 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     }
 
     // 4. support size and dropped mass with respect to tau_ref
-    int ns = 0;
+    // (every token above tau_ref is a candidate: tau_ref >= tau >= max - 1)
+    int ns = 0, nref = 0;
     float kept = 0.0f;
     const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+    const bool want_ref = delta_out || supref_out;
     if (!empty) each_cand([&](float x, int) {
         ns += x > tau ? 1 : 0;
-        if (delta_out && x > tref) kept += pw<MODE>(x - tref, beta);
+        if (want_ref && x > tref) {
+            kept += pw<MODE>(x - tref, beta);
+            ++nref;
+        }
     });
     const int sinc = wave_incl_scan(ns);
     const int nsw = __builtin_amdgcn_readlane(sinc, 63);      // this wave's support
     {
         float r[4];
         bool any;
-        head_sums((float)nsw, delta_out ? wave_sum(kept) : 0.0f, 0.0f, 0.0f, 0, r, any);
+        head_sums((float)nsw, want_ref ? wave_sum(kept) : 0.0f, want_ref ? (float)wave_isum(nref) : 0.0f, 0.0f, 0,
+                  r, any);
         if (w == 0 && lane == 0) {
             tau_out[oh] = empty ? -INFINITY : tau;
             if (support_out) support_out[oh] = empty ? 0 : (int32_t)r[0];
             if (delta_out) delta_out[oh] = empty ? 1.0f : 1.0f - r[1];
+            if (supref_out) supref_out[oh] = empty ? 0 : (int32_t)r[2];
         }
     }
 
@@ -878,7 +888,7 @@ template <typename T, int D, int R, int MODE>
 static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_cache, const int32_t* pt,
                             const int32_t* sl, const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
                             float alpha, float beta, const float* logits, const float* tau_ref, float* out,
-                            float* tau, int32_t* support, float* delta, hipStream_t s) {
+                            float* tau, int32_t* support, float* delta, int32_t* supref, hipStream_t s) {
     const int units = d.B * d.G;
     // KPL float4 of logits per lane in all; W = 16 / R waves per head, at most KPL.
     constexpr int WMAX = 16 / R;
@@ -887,7 +897,7 @@ static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_c
         constexpr int W = WMAX < KPL ? WMAX : KPL;                                                          \
         sparse_tau_pv_kernel<T, D, R, W, KPL / W, MODE><<<dim3(units), dim3(64 * R * W), 0, s>>>(           \
             (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
-            tau_ref, out, tau, support, delta);                                                             \
+            tau_ref, out, tau, support, delta, supref);                                                     \
         return hipGetLastError();                                                                           \
     }
     if (pl.nslot <= 256) EKV_FUSED(1)
@@ -903,7 +913,8 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
                              const void* v_cache, const int32_t* pt, const int32_t* sl,
                              const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
                              float alpha, int mode, float beta, const float* tau_ref, float* out,
-                             float* tau, int32_t* support, float* delta, char* ws, hipStream_t s) {
+                             float* tau, int32_t* support, float* delta, int32_t* supref, char* ws,
+                             hipStream_t s) {
     float* logits = (float*)(ws + pl.off_logits);
     float* part1 = (float*)(ws + pl.off_part1);
     float* part3 = (float*)(ws + pl.off_part3);
@@ -918,14 +929,14 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         switch (mode) {
             case kModeBeta1:
                 return run_fused<T, D, R, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, s);
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
             case kModeBeta2:
                 return run_fused<T, D, R, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, s);
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
             default:
                 return run_fused<T, D, R, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,
                                                         sel_stride, alpha, beta, logits, tau_ref, out, tau,
-                                                        support, delta, s);
+                                                        support, delta, supref, s);
         }
     }
     logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
@@ -935,7 +946,7 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
     if (e != hipSuccess) return e;
     tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
                                                      d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
-                                                     tau_ref, tau, support, delta);
+                                                     tau_ref, tau, support, delta, supref);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(
@@ -951,7 +962,7 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
                          float alpha, const float* tau_ref, float* out, float* tau,
-                         int32_t* support, float* delta, char* ws, hipStream_t s) {
+                         int32_t* support, float* delta, int32_t* supref, char* ws, hipStream_t s) {
     int mode;
     float beta = 0.0f;
     if (alpha == 1.0f) {
@@ -963,7 +974,7 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
 #define EKV_DEC(RR, T, DD)                                                                       \
     return run_decode<T, DD, RR>(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages,    \
                                  sel_count, sel_stride, alpha, mode, beta, tau_ref, out, tau,     \
-                                 support, delta, ws, s)
+                                 support, delta, supref, ws, s)
 #define EKV_RSW(T, DD)                          \
     switch (d.R) {                              \
         case 1: EKV_DEC(1, T, DD);              \

@@ -61,6 +61,6 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
                          float alpha, const float* tau_ref, float* out, float* tau,
-                         int32_t* support, float* delta, char* ws, hipStream_t s);
+                         int32_t* support, float* delta, int32_t* supref, char* ws, hipStream_t s);
 
 }  // namespace ekv

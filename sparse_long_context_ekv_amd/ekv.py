@@ -63,7 +63,7 @@ def load(path: str | None = None):
     lib.ekv_score_pages.argtypes = [sp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_select.argtypes = [sp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
-                                      _vp, _vp, _vp, _vp, _vp, _szp, _vp]
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ekv_last_error.restype = ctypes.c_char_p
@@ -149,18 +149,19 @@ def decode_workspace_bytes(shape, sparse: bool, sel_stride: int, alpha: float = 
     n = ctypes.c_size_t(0)
     dummy = 1 if sparse else None
     _check(load().ekv_entmax_decode(ctypes.byref(shape), None, None, None, None, None, dummy, dummy,
-                                    int(sel_stride), float(alpha), None, None, None, None, None, None,
+                                    int(sel_stride), float(alpha), None, None, None, None, None, None, None,
                                     ctypes.byref(n), None))
     return n.value
 
 
 def entmax_decode(shape, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count, sel_stride, alpha,
-                  out, tau, workspace, support=None, delta=None, tau_ref=None, stream=None):
+                  out, tau, workspace, support=None, delta=None, tau_ref=None, support_ref=None, stream=None):
     n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check(load().ekv_entmax_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                     _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count), int(sel_stride),
                                     float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau), _ptr(support),
-                                    _ptr(delta), _ptr(workspace), ctypes.byref(n), _stream(stream)))
+                                    _ptr(delta), _ptr(support_ref), _ptr(workspace), ctypes.byref(n),
+                                    _stream(stream)))
 
 
 # ------------------------------------------------------------- one step ----
@@ -264,11 +265,11 @@ class Decoder:
         select(self.shape, self.selector, self.wl.seq_lens, self.alpha, self.budget, self.z, b.score, b.mu,
                b.sigma, b.sel_pages, b.sel_count, b.tau_hat, b.ws_select, stream=stream)
 
-    def decode(self, stream=None, tau_ref=None, delta=None):
+    def decode(self, stream=None, tau_ref=None, delta=None, support_ref=None):
         wl, b = self.wl, self.buf
         entmax_decode(self.shape, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, b.sel_pages,
                       b.sel_count, self.budget, self.alpha, b.out, b.tau, b.ws_decode, support=b.support,
-                      delta=delta, tau_ref=tau_ref, stream=stream)
+                      delta=delta, tau_ref=tau_ref, support_ref=support_ref, stream=stream)
 
     def step(self, stream=None):
         self.score(stream)

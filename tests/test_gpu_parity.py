@@ -280,10 +280,12 @@ def _run_decode(wl, alpha, sel=None, cnt=None, stride=0, tau_ref=None):
     tau = torch.empty(c.batch, c.num_q_heads, device="cuda")
     sup = torch.empty(c.batch, c.num_q_heads, dtype=torch.int32, device="cuda")
     delta = torch.empty_like(tau) if tau_ref is not None else None
+    supref = torch.empty_like(sup) if tau_ref is not None else None
     ws = torch.empty(ekv.decode_workspace_bytes(sh, sel is not None, stride, alpha), dtype=torch.uint8, device="cuda")
     ekv.entmax_decode(sh, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, sel, cnt, stride, alpha,
-                      out, tau, ws, support=sup, delta=delta, tau_ref=tau_ref)
+                      out, tau, ws, support=sup, delta=delta, tau_ref=tau_ref, support_ref=supref)
     H.sync()
+    _run_decode.supref = supref
     return out, tau, sup, delta
 
 
@@ -328,7 +330,9 @@ def test_sparse_decode_on_oracle_selection(name, alpha):
         sels.append(res["sel"])
     sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, budget)
     _, tau_full, _, _ = _run_decode(wl, alpha)
+    _, _, sup_full, _ = _run_decode(wl, alpha)
     out, tau, sup, delta = _run_decode(wl, alpha, sel, cnt, budget, tau_ref=tau_full)
+    supref = _run_decode.supref
     r = c.num_q_heads // c.num_kv_groups
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
@@ -342,6 +346,13 @@ def test_sparse_decode_on_oracle_selection(name, alpha):
             assert abs(float(delta[b, h]) - d_or) <= H.DELTA_ATOL
             s_sel = full["s"][h][toks]
             assert abs(int(sup[b, h]) - int(sp["support"][h])) <= _support_slack(s_sel, sp["tau"][h], alpha)
+            # support recall rho: full-cache support tokens inside the selection
+            rho = oracle.decode.metrics(full, {"tokens": toks, "out": sp["out"]}, n)["rho"][h]
+            kept_or = int(round(rho * max(int(np.count_nonzero(full["p"][h] > 0)), 1)))
+            assert abs(int(supref[b, h]) - kept_or) <= _support_slack(s_sel, full["tau"][h], alpha), (b, h)
+            if alpha == 1.0:
+                assert int(supref[b, h]) == len(toks)          # softmax: rho is the coverage
+            assert int(supref[b, h]) <= int(sup_full[b, h]) + _support_slack(full["s"][h], full["tau"][h], alpha)
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama-ragged"])

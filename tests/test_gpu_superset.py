@@ -45,7 +45,8 @@ def test_superset_selection_is_exact(name, alpha):
     full = ekv.FullDecoder(wl, alpha)
     full.run()
     delta = torch.empty_like(dec.buf.tau)
-    dec.decode(tau_ref=full.tau, delta=delta)
+    supref = torch.empty_like(dec.buf.support)
+    dec.decode(tau_ref=full.tau, delta=delta, support_ref=supref)
     H.sync()
     tau_lo = H.to_np(dec.first["tau"])
     for b in range(c.batch):
@@ -83,3 +84,5 @@ def test_superset_selection_is_exact(name, alpha):
         for h in range(HQ):
             assert H.tau_close(float(dec.buf.tau[b, h]), ref_full["tau"][h])
             assert abs(float(delta[b, h])) <= H.DELTA_ATOL, (b, h, float(delta[b, h]))
+            # every full-cache support token is selected: rho = 1
+            assert int(supref[b, h]) == int(full.support[b, h]), (b, h)
