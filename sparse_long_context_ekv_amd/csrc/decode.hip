@@ -84,16 +84,21 @@ __global__ __launch_bounds__(256) void logits_kernel(
 
     for (int i = i0; i < i1; i += kLogitUnroll) {
         Vec<T, CH> kv[kLogitUnroll];
-        int lp[kLogitUnroll];
+        int lp[kLogitUnroll], phys[kLogitUnroll];
         bool ok[kLogitUnroll];
+        // Branch-free, so that all loads of the unroll are in flight at once
+        // (a load under a per-page branch waits for the previous ones); an
+        // empty slot reads page 0 and is ignored.
 #pragma unroll
         for (int u = 0; u < kLogitUnroll; ++u) {
-            const int ii = i + u;
-            lp[u] = ii < i1 ? sh_lp[ii - i0] : -1;
-            const int phys = ii < i1 ? sh_phys[ii - i0] : -1;
+            const int t = min(i + u - i0, ppb - 1);
+            lp[u] = i + u < i1 ? sh_lp[t] : -1;
+            phys[u] = sh_phys[t];
             ok[u] = lp[u] >= 0;
-            if (ok[u]) kv[u].load(k_cache + (((size_t)phys * G + g) * kPage + row) * D + lane * CH);
         }
+#pragma unroll
+        for (int u = 0; u < kLogitUnroll; ++u)
+            kv[u].load(k_cache + (((size_t)(ok[u] ? phys[u] : 0) * G + g) * kPage + row) * D + lane * CH);
 #pragma unroll
         for (int u = 0; u < kLogitUnroll; ++u) {
             const int ii = i + u;

@@ -72,16 +72,19 @@ __global__ __launch_bounds__(256) void box_score_kernel(
     for (int p0 = p_begin + slot; active && p0 < p_end; p0 += kUnroll * per_iter) {
         Vec<T, CH> lo[kUnroll], hi[kUnroll];
         bool ok[kUnroll];
+        int phys[kUnroll];
+        // All table entries, then all statistics loads, without branches, so
+        // that every load of the unroll is in flight at once (a load under a
+        // per-page branch waits for the previous ones).  Past the block's end
+        // or on a bad entry, page 0 is read and ignored.
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) phys[u] = pt[min(p0 + u * per_iter, p_end - 1)];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int p = p0 + u * per_iter;
-            int phys = p < p_end ? pt[p] : -1;
-            ok[u] = phys >= 0 && phys < NP;
-            if (ok[u]) {
-                const size_t off = ((size_t)phys * G + g) * D + lane * CH;
-                lo[u].load(kmin + off);
-                hi[u].load(kmax + off);
-            }
+            ok[u] = p0 + u * per_iter < p_end && phys[u] >= 0 && phys[u] < NP;
+            const size_t off = ((size_t)(ok[u] ? phys[u] : 0) * G + g) * D + lane * CH;
+            lo[u].load(kmin + off);
+            hi[u].load(kmax + off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -160,16 +163,16 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
     for (int p0 = p_begin + slot; active && p0 < p_end; p0 += kUnroll * per_iter) {
         Vec<S, CH> mv[kUnroll], vv[kUnroll];
         bool ok[kUnroll];
+        int phys[kUnroll];
+        // as in box_score_kernel: all loads of the unroll in flight at once
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) phys[u] = pt[min(p0 + u * per_iter, p_end - 1)];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int p = p0 + u * per_iter;
-            int phys = p < p_end ? pt[p] : -1;
-            ok[u] = phys >= 0 && phys < NP;
-            if (ok[u]) {
-                const size_t off = ((size_t)phys * G + g) * D + lane * CH;
-                mv[u].load(kmean + off);
-                vv[u].load(kvar + off);
-            }
+            ok[u] = p0 + u * per_iter < p_end && phys[u] >= 0 && phys[u] < NP;
+            const size_t off = ((size_t)(ok[u] ? phys[u] : 0) * G + g) * D + lane * CH;
+            mv[u].load(kmean + off);
+            vv[u].load(kvar + off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
