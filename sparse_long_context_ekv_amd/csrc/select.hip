@@ -233,26 +233,43 @@ __global__ __launch_bounds__(kTauThreads) void gauss_tau_kernel(
     float xmax = -INFINITY;
     const bool vec = staged && ((((uintptr_t)mrow) | ((uintptr_t)srow)) & 15) == 0;
     if (vec) {
-        for (int p4 = 4 * (int)threadIdx.x; p4 < M; p4 += 4 * kTauThreads) {
-            if (p4 + 4 <= M) {
-                const float4 m4 = *reinterpret_cast<const float4*>(mrow + p4);
-                const float4 s4 = *reinterpret_cast<const float4*>(srow + p4);
-                const float xm[4] = {a * m4.x, a * m4.y, a * m4.z, a * m4.w};
-                const float xs[4] = {a * s4.x, a * s4.y, a * s4.z, a * s4.w};
+        // All 16-byte loads first (at most kTauLdsPages / (4 kTauThreads) = 4
+        // per row and thread), with no branch between them, so that they are
+        // in flight together; chunks past the full ones read chunk 0 and are
+        // dropped.  Then the < 4 trailing pages one by one.
+        constexpr int NV = kTauLdsPages / (4 * kTauThreads);
+        const int nv = M >> 2;                   // full 4-page chunks
+        float4 m4[NV], s4[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = (int)threadIdx.x + k * kTauThreads;
+            const int cc = c < nv ? c : 0;
+            if (nv > 0) {                        // block-uniform
+                m4[k] = *reinterpret_cast<const float4*>(mrow + 4 * cc);
+                s4[k] = *reinterpret_cast<const float4*>(srow + 4 * cc);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = (int)threadIdx.x + k * kTauThreads;
+            if (c < nv) {
+                const float xm[4] = {a * m4[k].x, a * m4[k].y, a * m4[k].z, a * m4[k].w};
+                const float xs[4] = {a * s4[k].x, a * s4[k].y, a * s4[k].z, a * s4[k].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    const int p = 4 * c + i;
                     xmax = fmaxf(xmax, xm[i]);
-                    lds2[p4 + i] = make_float2(xm[i], xs[i]);
-                    if (((p4 + i) & (kTauSub - 1)) == 0) sub2[(p4 + i) / kTauSub] = make_float2(xm[i], xs[i]);
-                }
-            } else {
-                for (int p = p4; p < M; ++p) {
-                    const float xm = a * mrow[p];
-                    xmax = fmaxf(xmax, xm);
-                    lds2[p] = make_float2(xm, a * srow[p]);
-                    if ((p & (kTauSub - 1)) == 0) sub2[p / kTauSub] = lds2[p];
+                    lds2[p] = make_float2(xm[i], xs[i]);
+                    if ((p & (kTauSub - 1)) == 0) sub2[p / kTauSub] = make_float2(xm[i], xs[i]);
                 }
             }
+        }
+        const int p = 4 * nv + (int)threadIdx.x;
+        if (p < M) {
+            const float xm = a * mrow[p];
+            xmax = fmaxf(xmax, xm);
+            lds2[p] = make_float2(xm, a * srow[p]);
+            if ((p & (kTauSub - 1)) == 0) sub2[p / kTauSub] = lds2[p];
         }
     } else {
         for (int p = threadIdx.x; p < M; p += kTauThreads) {
