@@ -815,20 +815,19 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
             Vec<T, CH> vv[PVU];
             float pp[PVU];
             bool okv[PVU];
+            // Branch-free, so that the PVU row loads are in flight together
+            // (a load under a branch waits for the earlier ones); a slot past
+            // the list reads entry 0's row of page 0 and is ignored.
 #pragma unroll
             for (int u = 0; u < PVU; ++u) {
                 const int e = e0 + 4 * u + rg;
-                okv[u] = false;
-                pp[u] = 0.0f;
-                if (e < nent) {
-                    const int slot = ls[e];
-                    const int phys = phys_of[slot >> 4];
-                    if (phys >= 0) {
-                        okv[u] = true;
-                        pp[u] = lpv[e];
-                        vv[u].load(v_cache + (((size_t)phys * G + g) * kPage + (slot & (kPage - 1))) * D + l16 * CH);
-                    }
-                }
+                const int ec = e < nent ? e : 0;
+                const int slot = ls[ec];
+                const int phys = phys_of[slot >> 4];
+                okv[u] = e < nent && phys >= 0;
+                pp[u] = okv[u] ? lpv[ec] : 0.0f;
+                vv[u].load(v_cache + (((size_t)(okv[u] ? phys : 0) * G + g) * kPage + (slot & (kPage - 1))) * D +
+                           l16 * CH);
             }
 #pragma unroll
             for (int u = 0; u < PVU; ++u)
