@@ -99,6 +99,29 @@ def test_page_stats_fp8_storage():
         np.testing.assert_array_equal(got, want)
 
 
+def test_page_stats_fp8_storage_d64():
+    """The same on d = 64 with fp32 keys (each lane's slice of a statistic
+    is then one 4-byte word), and Gaussian moments on the stored values."""
+    wl = workload("tiny")
+    c = wl.cfg
+    st32 = _stats(wl, "f32")
+    st8 = _stats(wl, "fp8")
+    mu = torch.empty(c.batch, c.num_q_heads, wl.max_pages, device="cuda")
+    sg = torch.empty_like(mu)
+    ekv.score_pages(_shape(wl, "fp8"), ekv.SEL_GAUSS, wl.q, wl.page_table, wl.seq_lens, kmean=st8["kmean"],
+                    kvar=st8["kvar"], mu=mu, sigma=sg)
+    H.sync()
+    for key in ("kmean", "kvar"):
+        want = oracle.paged.round_fp8_e4m3(H.to_np(st32[key]))
+        np.testing.assert_array_equal(st8[key].cpu().to(torch.float64).numpy(), want)
+    q = H.to_np(wl.q[0])
+    mean, var = _stored_stats_logical(st8, wl, 0)
+    omu, osg = oracle.paged.gauss_moments(q, mean, var)
+    M = omu.shape[1]
+    np.testing.assert_allclose(H.to_np(mu[0, :, :M]), omu, rtol=1e-5, atol=1e-5 * np.abs(omu).max())
+    np.testing.assert_allclose(H.to_np(sg[0, :, :M]), osg, rtol=1e-5, atol=1e-5 * np.abs(osg).max())
+
+
 def _stored_stats_logical(st, wl, b):
     """The stored mean/var of sequence b, up-cast exactly, in logical page order."""
     rows = H.phys_rows(wl, b)
@@ -285,8 +308,7 @@ def _run_decode(wl, alpha, sel=None, cnt=None, stride=0, tau_ref=None):
     ekv.entmax_decode(sh, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, sel, cnt, stride, alpha,
                       out, tau, ws, support=sup, delta=delta, tau_ref=tau_ref, support_ref=supref)
     H.sync()
-    _run_decode.supref = supref
-    return out, tau, sup, delta
+    return out, tau, sup, delta, supref
 
 
 def _support_slack(s_row, tau, alpha):
@@ -302,7 +324,7 @@ def _support_slack(s_row, tau, alpha):
 def test_full_cache_decode(name, alpha):
     wl = workload(name)
     c = wl.cfg
-    out, tau, sup, _ = _run_decode(wl, alpha)
+    out, tau, sup, _, _ = _run_decode(wl, alpha)
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
         ref = oracle.decode.decode(q, K, V, None, alpha)
@@ -329,10 +351,8 @@ def test_sparse_decode_on_oracle_selection(name, alpha):
         res = oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", alpha, budget)
         sels.append(res["sel"])
     sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, budget)
-    _, tau_full, _, _ = _run_decode(wl, alpha)
-    _, _, sup_full, _ = _run_decode(wl, alpha)
-    out, tau, sup, delta = _run_decode(wl, alpha, sel, cnt, budget, tau_ref=tau_full)
-    supref = _run_decode.supref
+    _, tau_full, sup_full, _, _ = _run_decode(wl, alpha)
+    out, tau, sup, delta, supref = _run_decode(wl, alpha, sel, cnt, budget, tau_ref=tau_full)
     r = c.num_q_heads // c.num_kv_groups
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
