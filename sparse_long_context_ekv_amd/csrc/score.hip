@@ -17,7 +17,7 @@
 // A block covers 2^lg_ppb consecutive logical pages of one sequence (up to
 // 256); each row issues the loads of UNROLL pages before using any of them.
 // Results are staged in LDS and written once, at the end of the block, one
-// contiguous run of pages per output row: single-float stores scattered over
+// contiguous run of pages per output row, four floats per store: single-float stores scattered over
 // the [B][.][MP] rows (one per page and head) cost the statistics stream a
 // third of its speed, and stores interleaved with the stream cost twice what
 // they cost alone.
@@ -28,11 +28,36 @@ namespace ekv {
 
 constexpr int kUnroll = 4;
 
+// Writes a block's staged results, rows of 2^lg floats in LDS, to output
+// rows starting at column p_begin, np columns of each.  One thread moves four
+// consecutive columns (a 16-byte LDS read and, where the destination is
+// 16-byte aligned, one 16-byte store): the flush is the tail of every block,
+// and single-float copies made it several times longer.
+template <typename RowPtr>
+__device__ __forceinline__ void flush_rows(const float* stage, int nrows, int lg, int p_begin, int np,
+                                           bool vec, RowPtr row_ptr) {
+    const int lq = lg - 2;                     // quads per row, log2 (lg >= 2)
+    for (int i = threadIdx.x; i < (nrows << lq); i += blockDim.x) {
+        const int rr = i >> lq, pp = (i & ((1 << lq) - 1)) << 2;
+        if (pp >= np) continue;
+        const float4 v = *reinterpret_cast<const float4*>(stage + (i << 2));
+        float* o = row_ptr(rr) + p_begin + pp;
+        if (vec && pp + 4 <= np) {
+            *reinterpret_cast<float4*>(o) = v;
+        } else {
+            o[0] = v.x;
+            if (pp + 1 < np) o[1] = v.y;
+            if (pp + 2 < np) o[2] = v.z;
+            if (pp + 3 < np) o[3] = v.w;
+        }
+    }
+}
+
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void box_score_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const T* __restrict__ kmin, const T* __restrict__ kmax,
-    float* __restrict__ score, int G, int MP, int NP, int lg_ppb, float inv_sqrt_d) {
+    float* __restrict__ score, int G, int MP, int NP, int lg_ppb, float inv_sqrt_d, bool vec) {
     constexpr int CH = D / kRow;
     extern __shared__ float stage[];           // [G][ppb]
     const int ppb = 1 << lg_ppb;
@@ -115,11 +140,8 @@ __global__ __launch_bounds__(256) void box_score_kernel(
         }
     }
     __syncthreads();
-    const int np = p_end - p_begin;
-    for (int i = threadIdx.x; i < (G << lg_ppb); i += blockDim.x) {
-        const int gg = i >> lg_ppb, pp = i & (ppb - 1);
-        if (pp < np) score[((size_t)b * G + gg) * MP + p_begin + pp] = stage[i];
-    }
+    flush_rows(stage, G, lg_ppb, p_begin, p_end - p_begin, vec,
+               [&](int gg) { return score + ((size_t)b * G + gg) * MP; });
 }
 
 template <typename T, typename S, int D, int R>
@@ -127,7 +149,7 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const S* __restrict__ kmean, const S* __restrict__ kvar,
     float* __restrict__ mu, float* __restrict__ sigma, int G, int MP, int NP, int lg_ppb,
-    float inv_sqrt_d, float inv_d) {
+    float inv_sqrt_d, float inv_d, bool vec) {
     constexpr int CH = D / kRow;
     extern __shared__ float stage[];           // [2][HQ][ppb]: mu, then sigma
     const int ppb = 1 << lg_ppb;
@@ -195,12 +217,9 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
         }
     }
     __syncthreads();
-    const int np = p_end - p_begin;
-    for (int i = threadIdx.x; i < (2 * HQ) << lg_ppb; i += blockDim.x) {
-        const int hh = i >> lg_ppb, pp = i & (ppb - 1);
-        float* o = hh < HQ ? mu + ((size_t)b * HQ + hh) * MP : sigma + ((size_t)b * HQ + hh - HQ) * MP;
-        if (pp < np) o[p_begin + pp] = stage[i];
-    }
+    flush_rows(stage, 2 * HQ, lg_ppb, p_begin, p_end - p_begin, vec, [&](int hh) {
+        return hh < HQ ? mu + ((size_t)b * HQ + hh) * MP : sigma + ((size_t)b * HQ + hh - HQ) * MP;
+    });
 }
 
 // log2 of the pages per block.  Measured on the 128K batched workload: with
@@ -238,8 +257,9 @@ static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const
     if (((size_t)d.G << lg) * sizeof(float) > 48 * 1024 && !allow_64k_lds(box_score_kernel<T, D, R>)) lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
     const size_t lds = ((size_t)d.G << lg) * sizeof(float);
+    const bool vec = d.MP % 4 == 0 && ((uintptr_t)score & 15) == 0;
     box_score_kernel<T, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const T*)kmin, (const T*)kmax,
-                                                           score, d.G, d.MP, d.NP, lg, 1.0f / sqrtf((float)D));
+                                                           score, d.G, d.MP, d.NP, lg, 1.0f / sqrtf((float)D), vec);
     return hipGetLastError();
 }
 
@@ -251,9 +271,10 @@ static hipError_t run_gauss(const Dims& d, const void* q, const int32_t* pt, con
         lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
     const size_t lds = ((size_t)2 * d.HQ << lg) * sizeof(float);
+    const bool vec = d.MP % 4 == 0 && ((uintptr_t)mu & 15) == 0 && ((uintptr_t)sigma & 15) == 0;
     gauss_score_kernel<T, S, D, R><<<grid, dim3(256), lds, s>>>((const T*)q, pt, sl, (const S*)kmean,
                                                                 (const S*)kvar, mu, sigma, d.G, d.MP, d.NP, lg,
-                                                                1.0f / sqrtf((float)D), 1.0f / (float)D);
+                                                                1.0f / sqrtf((float)D), 1.0f / (float)D, vec);
     return hipGetLastError();
 }
 
