@@ -158,7 +158,7 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
     }
     if (superset && !(alpha > 1.0f)) return fail(EKV_ERR_INVALID_ARG, "superset selection needs alpha > 1 (got %g)", alpha);
     if (superset && !(alpha < 1e6f)) return fail(EKV_ERR_INVALID_ARG, "alpha out of range (got %g)", alpha);
-    const size_t keys_bytes = align256((size_t)d.B * d.G * d.MP * sizeof(uint32_t));
+    const size_t keys_bytes = align256(ekv::select_keys_bytes(d, budget_pages));
     const size_t tau_bytes = gauss ? align256((size_t)d.B * d.HQ * sizeof(float)) : 0;
     const size_t need = keys_bytes + tau_bytes;
     if (!workspace) {

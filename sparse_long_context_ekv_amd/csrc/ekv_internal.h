@@ -36,9 +36,10 @@ hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_
                               float* mu, float* sigma, hipStream_t s);
 
 // Selection.  mode: 0 top-k, 1 Gaussian, 2 support superset (ekv_selector).
-// `keys` is workspace [B][G][MP] uint32.
+// `keys` is workspace of select_keys_bytes(d, budget) bytes (256-byte aligned).
 hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
                             const int32_t* seq_lens, float alpha, float* tau_hat, hipStream_t s);
+size_t select_keys_bytes(const Dims& d, int budget);
 hipError_t launch_select(const Dims& d, int mode, const int32_t* seq_lens, float alpha,
                          int budget, float z, const float* score, const float* mu,
                          const float* sigma, const float* tau_hat, uint32_t* keys,

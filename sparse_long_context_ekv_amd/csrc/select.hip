@@ -496,26 +496,15 @@ __device__ __forceinline__ void load_span(const float* __restrict__ row, int p0,
     }
 }
 
-// Same selection as select_kernel with the keys held in registers: thread t
-// owns the KPT consecutive pages [t*KPT, (t+1)*KPT), so one block-wide scan of
-// per-thread counts places every kept page in ascending order.  Needs
-// M <= KPT * kSelThreads.
+// Keys of the KPT consecutive pages [p0, p0 + KPT) of row (b, g): the pooled
+// box score (top-k, superset) or the pooled Gaussian margin.  Entries at or
+// past M are filled but never used.
 template <int MODE, int R, int KPT>
-__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
-    const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
-    const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
-    float inv_a, float zcut, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
-    __shared__ int hist[256];
-    __shared__ int wsum[3 * kSelWaves];
-    __shared__ int sh_digit, sh_above;
-    const int g = blockIdx.x, b = blockIdx.y;
+__device__ __forceinline__ void page_keys(const float* __restrict__ score, const float* __restrict__ mu,
+                                          const float* __restrict__ sigma, const float* __restrict__ tau_hat,
+                                          float inv_a, int b, int g, int G, int MP, int M, int p0,
+                                          uint32_t (&key)[KPT]) {
     const int HQ = G * R;
-    const int M = num_pages(seq_len_at(seq_lens, b, MP));
-    int32_t* out = sel_pages + ((size_t)b * G + g) * budget;
-    const int p0 = threadIdx.x * KPT;
-
-    // Keys: pooled box score, or pooled Gaussian margin.
-    uint32_t key[KPT];
     if constexpr (MODE == kSelGauss) {
         constexpr int C = KPT < 8 ? KPT : 8;      // pages per sub-chunk (bounds registers)
 #pragma unroll
@@ -547,97 +536,98 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
 #pragma unroll
         for (int i = 0; i < KPT; ++i) key[i] = ord_key(f[i]);
     }
+}
 
-    // Candidates (key >= cut): their count and key range.
-    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
-    int cnt = 0;
-    uint32_t cmin = 0xffffffffu, cmax = 0u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        if (p0 + i < M && key[i] >= cut) {
-            ++cnt;
-            cmin = min(cmin, key[i]);
-            cmax = max(cmax, key[i]);
-        }
-    }
-    int ncand;
-    block_count_range<kSelWaves>(cnt, cmin, cmax, &ncand, wsum);
-    const int keep = M == 0 ? 0 : max(1, min(budget, ncand));
-
-    uint32_t T;
-    int need_eq;
-    if (ncand >= 1 && ncand <= budget) {
+// The cutoff (T, need_eq) of a block-wide selection over keys in registers:
+// the kept entries are those with key > T, then the first need_eq with
+// key == T in entry order.  `ok(i)` tells which register entries exist.
+// `ncand` is the number of keys at or above `cut` (the candidates) and
+// `keep` the number to keep; with 1 <= ncand <= keep every candidate is kept.
+// Otherwise the keep-th largest key is found by an 8-bit radix select; when
+// ncand > keep the answer is a candidate, so only candidates are
+// histogrammed, as offsets from the smallest (cmin; cmax the largest), and
+// the first pass takes the top 8 bits of the candidates' own range.
+// (ncand == 0: over every key.)
+template <int KPT, typename Ok>
+__device__ __forceinline__ void block_kth_key(const uint32_t (&key)[KPT], Ok ok, uint32_t cut, int ncand, int keep,
+                                              uint32_t cmin, uint32_t cmax, int* hist, int* sh_digit,
+                                              int* sh_above, uint32_t& T, int& need_eq) {
+    if (ncand >= 1 && ncand <= keep) {
         T = cut;              // every candidate, nothing else
-        need_eq = M;
-    } else if (keep > 0) {
-        // Radix select of the keep-th largest key.  With ncand > budget the
-        // answer is a candidate, so only candidates are histogrammed, as
-        // offsets from the smallest; the first pass takes the top 8 bits of
-        // the candidates' own range, spreading them over the 256 bins.
-        // (ncand == 0 keeps one page: the largest key of all.)
-        const bool all = ncand == 0;
-        const uint32_t base = all ? 0u : cmin;
-        const uint32_t span = all ? 0xffffffffu : cmax - cmin;
-        const int nbits = span ? 32 - __builtin_clz(span) : 0;
-        uint32_t prefix = 0;     // determined high bits of (key - base)
-        int remaining = keep;
-        int shift = nbits > 8 ? nbits - 8 : 0;
-        int width = nbits > 8 ? 8 : nbits;
-        while (width > 0) {
-            for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
-            __syncthreads();
-            const int top = shift + width;
-            const uint32_t hmask = top >= 32 ? 0u : (0xffffffffu << top);
-            const uint32_t dmask = (1u << width) - 1u;
-#pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-                const uint32_t rel = key[i] - base;
-                if (p0 + i < M && (all || key[i] >= cut) && (rel & hmask) == prefix)
-                    atomicAdd(&hist[(rel >> shift) & dmask], 1);
-            }
-            __syncthreads();
-            if (threadIdx.x < 64) {
-                // Lane l holds digits 255-4l .. 252-4l (descending); the first
-                // lane whose inclusive count reaches `remaining` walks its four.
-                const int l = threadIdx.x;
-                int c4[4], sum = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    c4[i] = hist[255 - 4 * l - i];
-                    sum += c4[i];
-                }
-                const int incl = wave_incl_scan(sum);
-                const uint64_t hit = __ballot(incl >= remaining);
-                const int L = hit ? (int)__builtin_ctzll(hit) : 63;
-                if (l == L) {
-                    int above = incl - sum, dgt = 255 - 4 * l - 3;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (above + c4[i] >= remaining) { dgt = 255 - 4 * l - i; break; }
-                        above += c4[i];
-                    }
-                    sh_digit = dgt;
-                    sh_above = above;
-                }
-            }
-            __syncthreads();
-            prefix |= (uint32_t)sh_digit << shift;
-            remaining -= sh_above;
-            width = shift >= 8 ? 8 : shift;
-            shift -= width;
-        }
-        T = base + prefix;
-        need_eq = remaining;
-    } else {
+        need_eq = 0x7fffffff;
+        return;
+    }
+    if (keep <= 0) {
         T = 0xffffffffu;
         need_eq = 0;
+        return;
     }
+    const bool all = ncand == 0;
+    const uint32_t base = all ? 0u : cmin;
+    const uint32_t span = all ? 0xffffffffu : cmax - cmin;
+    const int nbits = span ? 32 - __builtin_clz(span) : 0;
+    uint32_t prefix = 0;     // determined high bits of (key - base)
+    int remaining = keep;
+    int shift = nbits > 8 ? nbits - 8 : 0;
+    int width = nbits > 8 ? 8 : nbits;
+    while (width > 0) {
+        for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        const int top = shift + width;
+        const uint32_t hmask = top >= 32 ? 0u : (0xffffffffu << top);
+        const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const uint32_t rel = key[i] - base;
+            if (ok(i) && (all || key[i] >= cut) && (rel & hmask) == prefix)
+                atomicAdd(&hist[(rel >> shift) & dmask], 1);
+        }
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            // Lane l holds digits 255-4l .. 252-4l (descending); the first
+            // lane whose inclusive count reaches `remaining` walks its four.
+            const int l = threadIdx.x;
+            int c4[4], sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c4[i] = hist[255 - 4 * l - i];
+                sum += c4[i];
+            }
+            const int incl = wave_incl_scan(sum);
+            const uint64_t hit = __ballot(incl >= remaining);
+            const int L = hit ? (int)__builtin_ctzll(hit) : 63;
+            if (l == L) {
+                int above = incl - sum, dgt = 255 - 4 * l - 3;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (above + c4[i] >= remaining) { dgt = 255 - 4 * l - i; break; }
+                    above += c4[i];
+                }
+                *sh_digit = dgt;
+                *sh_above = above;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)*sh_digit << shift;
+        remaining -= *sh_above;
+        width = shift >= 8 ? 8 : shift;
+        shift -= width;
+    }
+    T = base + prefix;
+    need_eq = remaining;
+}
 
-    // Compaction in page order: keys > T, then the first need_eq keys == T.
+// Compaction of the kept entries in entry order (thread t owns entries
+// [t*KPT, (t+1)*KPT)): one block-wide scan of per-thread counts gives each
+// kept entry its position; put(i, pos) is called for every kept entry with
+// pos < cap.  Returns min(kept, cap) (block-uniform).
+template <int KPT, typename Ok, typename Put>
+__device__ __forceinline__ int block_compact(const uint32_t (&key)[KPT], Ok ok, uint32_t T, int need_eq, int cap,
+                                             int* wsum, Put put) {
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        if (p0 + i < M) {
+        if (ok(i)) {
             ngt += key[i] > T ? 1 : 0;
             neq += key[i] == T ? 1 : 0;
         }
@@ -648,17 +638,181 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     int eq_rank = eeq;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        if (p0 + i < M) {
+        if (ok(i)) {
             const bool eq = key[i] == T;
             const bool take = key[i] > T || (eq && eq_rank < need_eq);
             eq_rank += eq ? 1 : 0;
             if (take) {
-                if (pos < budget) out[pos] = p0 + i;
+                if (pos < cap) put(i, pos);
                 ++pos;
             }
         }
     }
-    const int written = min(tgt + min(teq, need_eq), budget);
+    return min(tgt + min(teq, need_eq), cap);
+}
+
+// Candidates among the valid register keys (key >= cut): their count (block
+// total, every thread) and key range.
+template <int KPT, typename Ok>
+__device__ __forceinline__ int block_candidates(const uint32_t (&key)[KPT], Ok ok, uint32_t cut, uint32_t& cmin,
+                                                uint32_t& cmax, int* wsum) {
+    int cnt = 0;
+    cmin = 0xffffffffu;
+    cmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (ok(i) && key[i] >= cut) {
+            ++cnt;
+            cmin = min(cmin, key[i]);
+            cmax = max(cmax, key[i]);
+        }
+    }
+    int ncand;
+    block_count_range<kSelWaves>(cnt, cmin, cmax, &ncand, wsum);
+    return ncand;
+}
+
+// Same selection as select_kernel with the keys held in registers: thread t
+// owns the KPT consecutive pages [t*KPT, (t+1)*KPT), so one block-wide scan of
+// per-thread counts places every kept page in ascending order.  Needs
+// M <= KPT * kSelThreads.
+template <int MODE, int R, int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
+    const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
+    const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
+    float inv_a, float zcut, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
+    __shared__ int hist[256];
+    __shared__ int wsum[3 * kSelWaves];
+    __shared__ int sh_digit, sh_above;
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int HQ = G * R;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    int32_t* out = sel_pages + ((size_t)b * G + g) * budget;
+    const int p0 = threadIdx.x * KPT;
+    auto ok = [&](int i) { return p0 + i < M; };
+
+    uint32_t key[KPT];
+    page_keys<MODE, R, KPT>(score, mu, sigma, tau_hat, inv_a, b, g, G, MP, M, p0, key);
+    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
+    uint32_t cmin, cmax;
+    const int ncand = block_candidates<KPT>(key, ok, cut, cmin, cmax, wsum);
+    const int keep = M == 0 ? 0 : max(1, min(budget, ncand));
+    uint32_t T;
+    int need_eq;
+    block_kth_key<KPT>(key, ok, cut, ncand, keep, cmin, cmax, hist, &sh_digit, &sh_above, T, need_eq);
+    const int written = block_compact<KPT>(key, ok, T, need_eq, budget, wsum,
+                                           [&](int i, int pos) { out[pos] = p0 + i; });
+    for (int i = written + threadIdx.x; i < budget; i += kSelThreads) out[i] = -1;
+    if (threadIdx.x == 0) sel_count[(size_t)b * G + g] = written;
+}
+
+// Two-level selection for rows of many pages when there are few (sequence,
+// group) rows to spread over the chip.  Under the order "larger key first,
+// then lower page index", a page among the row's top `keep` is also among
+// the top `keep` of any subset that contains it, in particular of its own
+// chunk of kChunkPages pages.  So:
+//  select_chunk_kernel (grid: chunks x G x B) keeps the top min(budget,
+//    chunk) pages of each chunk, whatever the cutoff, as (key, page) entries
+//    in page order, and counts the chunk's candidates (keys at or above the
+//    cutoff);
+//  select_merge_kernel (grid: G x B) applies the one-level rule (keep =
+//    max(1, min(budget, candidates of the row))) to the union of the chunks'
+//    entries.  The union is in page order, so ties still go to the lower page
+//    and the output is ascending.
+// The result is the one-level selection exactly.  Workspace per row:
+// nchunk x budget entries (uint32 key, uint32 page), then nchunk counts
+// (entries kept, candidates).
+constexpr int kChunkPages = 4 * kSelThreads;
+constexpr int kMergeMaxChunks = 256;       // chunks per row at most
+constexpr int kMergeMaxEntries = 64 * kSelThreads;
+constexpr int kTwoLevelRows = 256;         // two-level only below this many rows ...
+constexpr int kTwoLevelMinPages = 8192;    // ... of more than this many pages
+
+template <int MODE, int R>
+__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(
+    const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ score,
+    const float* __restrict__ mu, const float* __restrict__ sigma, const float* __restrict__ tau_hat,
+    float inv_a, float zcut, int nchunk, uint2* __restrict__ entries, int2* __restrict__ counts) {
+    constexpr int KPT = kChunkPages / kSelThreads;
+    __shared__ int hist[256];
+    __shared__ int wsum[3 * kSelWaves];
+    __shared__ int sh_digit, sh_above;
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int HQ = G * R;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const size_t row = ((size_t)b * G + g) * nchunk + c;
+    uint2* out = entries + row * budget;
+    const int p0 = c * kChunkPages + threadIdx.x * KPT;
+    auto ok = [&](int i) { return p0 + i < M; };
+
+    uint32_t key[KPT];
+    page_keys<MODE, R, KPT>(score, mu, sigma, tau_hat, inv_a, b, g, G, MP, M, p0, key);
+    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
+    uint32_t cmin, cmax;
+    const int ncand = block_candidates<KPT>(key, ok, cut, cmin, cmax, wsum);
+    // The chunk's own top pages: here every valid page counts as a candidate.
+    uint32_t amin, amax;
+    const int nvalid = block_candidates<KPT>(key, ok, 0u, amin, amax, wsum);
+    const int keep = min(budget, nvalid);
+    uint32_t T;
+    int need_eq;
+    block_kth_key<KPT>(key, ok, 0u, nvalid, keep, amin, amax, hist, &sh_digit, &sh_above, T, need_eq);
+    const int written = block_compact<KPT>(key, ok, T, need_eq, budget, wsum, [&](int i, int pos) {
+        out[pos] = make_uint2(key[i], (uint32_t)(p0 + i));
+    });
+    if (threadIdx.x == 0) counts[row] = make_int2(written, ncand);
+}
+
+template <int MODE, int R, int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_merge_kernel(
+    const int32_t* __restrict__ seq_lens, int G, int MP, int budget, const float* __restrict__ tau_hat,
+    float inv_a, float zcut, int nchunk, const uint2* __restrict__ entries, const int2* __restrict__ counts,
+    int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
+    __shared__ int hist[256];
+    __shared__ int wsum[3 * kSelWaves];
+    __shared__ int sh_digit, sh_above;
+    __shared__ int sh_kept[kMergeMaxChunks];
+    __shared__ int sh_ncand;
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int HQ = G * R;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const size_t row0 = ((size_t)b * G + g) * nchunk;
+    int32_t* out = sel_pages + ((size_t)b * G + g) * budget;
+    if (threadIdx.x < 64) {
+        int nc = 0;
+        for (int c = threadIdx.x; c < nchunk; c += 64) {
+            const int2 k = counts[row0 + c];
+            sh_kept[c] = k.x;
+            nc += k.y;
+        }
+        nc = wave_isum(nc);
+        if (threadIdx.x == 0) sh_ncand = nc;
+    }
+    __syncthreads();
+    // Entry e = c * budget + i (chunk c, its i-th kept page): thread t owns
+    // entries [t*KPT, (t+1)*KPT); slots past a chunk's kept count are empty.
+    const int e0 = threadIdx.x * KPT;
+    uint32_t key[KPT], page[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int e = e0 + i;
+        const int c = e / budget;
+        const bool v = c < nchunk && e - c * budget < sh_kept[c < nchunk ? c : 0];
+        const uint2 x = v ? entries[row0 * budget + e] : make_uint2(0u, 0u);
+        key[i] = x.x;
+        page[i] = v ? x.y : 0xffffffffu;
+    }
+    auto ok = [&](int i) { return page[i] != 0xffffffffu; };
+    const uint32_t cut = select_cut<MODE, R>(tau_hat, (size_t)b * HQ + g * R, inv_a, zcut);
+    uint32_t cmin, cmax;
+    (void)block_candidates<KPT>(key, ok, cut, cmin, cmax, wsum);
+    const int ncand = sh_ncand;
+    const int keep = M == 0 ? 0 : max(1, min(budget, ncand));
+    uint32_t T;
+    int need_eq;
+    block_kth_key<KPT>(key, ok, cut, ncand, keep, cmin, cmax, hist, &sh_digit, &sh_above, T, need_eq);
+    const int written = block_compact<KPT>(key, ok, T, need_eq, budget, wsum,
+                                           [&](int i, int pos) { out[pos] = (int32_t)page[i]; });
     for (int i = written + threadIdx.x; i < budget; i += kSelThreads) out[i] = -1;
     if (threadIdx.x == 0) sel_count[(size_t)b * G + g] = written;
 }
@@ -701,12 +855,79 @@ hipError_t launch_gauss_tau(const Dims& d, const float* mu, const float* sigma,
     }
 }
 
+// Two-level selection (see select_chunk_kernel) when there are fewer rows
+// than half the compute units' worth and rows are long: one block per row
+// would leave most of the chip idle (65536-page rows of 8 groups took 71 us
+// in one level, measured).  Needs a budget well below the chunk, and the
+// chunks' entries of a row within the merge kernel's registers.
+static int two_level_chunks(const Dims& d, int budget) {
+    if ((long)d.B * d.G >= kTwoLevelRows || d.MP <= kTwoLevelMinPages || budget * 4 > kChunkPages) return 0;
+    const int nchunk = (d.MP + kChunkPages - 1) / kChunkPages;
+    if (nchunk > kMergeMaxChunks || (long)nchunk * budget > kMergeMaxEntries) return 0;
+    return nchunk;
+}
+
+size_t select_keys_bytes(const Dims& d, int budget) {
+    const size_t one = (size_t)d.B * d.G * d.MP * sizeof(uint32_t);
+    const int nchunk = two_level_chunks(d, budget);
+    const size_t rows = (size_t)d.B * d.G * nchunk;
+    const size_t two = nchunk ? ((rows * budget * sizeof(uint2) + 255) & ~(size_t)255) + rows * sizeof(int2) : 0;
+    return one > two ? one : two;
+}
+
 hipError_t launch_select(const Dims& d, int mode, const int32_t* seq_lens, float alpha,
                          int budget, float z, const float* score, const float* mu,
                          const float* sigma, const float* tau_hat, uint32_t* keys,
                          int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
     const float inv_a = alpha > 1.0f ? 1.0f / (alpha - 1.0f) : 0.0f;
     dim3 grid(d.G, d.B);
+    const int nchunk = two_level_chunks(d, budget);
+    if (nchunk) {
+        const size_t rows = (size_t)d.B * d.G * nchunk;
+        uint2* entries = reinterpret_cast<uint2*>(keys);
+        int2* counts = reinterpret_cast<int2*>(reinterpret_cast<char*>(keys) +
+                                               ((rows * budget * sizeof(uint2) + 255) & ~(size_t)255));
+        int kpt = 4;
+        while ((long)kpt * kSelThreads < (long)nchunk * budget) kpt *= 2;
+        const dim3 grid1(nchunk, d.G, d.B);
+#define EKV_TWO(MM, RR)                                                                                        \
+    {                                                                                                          \
+        select_chunk_kernel<MM, RR><<<grid1, dim3(kSelThreads), 0, s>>>(seq_lens, d.G, d.MP, budget, score,    \
+                                                                        mu, sigma, tau_hat, inv_a, z, nchunk,  \
+                                                                        entries, counts);                      \
+        switch (kpt) {                                                                                         \
+            case 4: select_merge_kernel<MM, RR, 4><<<grid, dim3(kSelThreads), 0, s>>>(                         \
+                        seq_lens, d.G, d.MP, budget, tau_hat, inv_a, z, nchunk, entries, counts, sel_pages,    \
+                        sel_count); break;                                                                     \
+            case 8: select_merge_kernel<MM, RR, 8><<<grid, dim3(kSelThreads), 0, s>>>(                         \
+                        seq_lens, d.G, d.MP, budget, tau_hat, inv_a, z, nchunk, entries, counts, sel_pages,    \
+                        sel_count); break;                                                                     \
+            case 16: select_merge_kernel<MM, RR, 16><<<grid, dim3(kSelThreads), 0, s>>>(                       \
+                        seq_lens, d.G, d.MP, budget, tau_hat, inv_a, z, nchunk, entries, counts, sel_pages,    \
+                        sel_count); break;                                                                     \
+            case 32: select_merge_kernel<MM, RR, 32><<<grid, dim3(kSelThreads), 0, s>>>(                       \
+                        seq_lens, d.G, d.MP, budget, tau_hat, inv_a, z, nchunk, entries, counts, sel_pages,    \
+                        sel_count); break;                                                                     \
+            default: select_merge_kernel<MM, RR, 64><<<grid, dim3(kSelThreads), 0, s>>>(                       \
+                        seq_lens, d.G, d.MP, budget, tau_hat, inv_a, z, nchunk, entries, counts, sel_pages,    \
+                        sel_count); break;                                                                     \
+        }                                                                                                      \
+        return hipGetLastError();                                                                              \
+    }
+#define EKV_TWOM(MM)                                         \
+    switch (d.R) {                                           \
+        case 1: EKV_TWO(MM, 1)                               \
+        case 2: EKV_TWO(MM, 2)                               \
+        case 4: EKV_TWO(MM, 4)                               \
+        case 8: EKV_TWO(MM, 8)                               \
+        default: return hipErrorInvalidValue;                \
+    }
+        if (mode == kSelGauss) { EKV_TWOM(kSelGauss) }
+        if (mode == kSelSuperset) { EKV_TWOM(kSelSuperset) }
+        EKV_TWO(kSelTopk, 1)
+#undef EKV_TWOM
+#undef EKV_TWO
+    }
     // Keys in registers when every sequence fits KPT * kSelThreads pages.
     int kpt = 0;
     for (int k = 4; k <= 64; k *= 2)

@@ -1,7 +1,8 @@
 """GPU parity of ekv_select on its own, against the fp64 oracle, at page
-counts that reach every kernel variant (keys in registers at 4..64 keys per
-thread, and the global-memory path beyond 65536 pages), with ragged and empty
-sequences and exact ties.  Selection rules: "EntmaxKV: Support-Aware Decoding
+counts and row counts that reach every kernel variant (one level: keys in
+registers at 4..64 keys per thread, and the global-memory path beyond 65536
+pages; two levels, chunk + merge, for few rows of more than 8192 pages), with
+ragged and empty sequences and exact ties.  Selection rules: "EntmaxKV: Support-Aware Decoding
 for Entmax Attention" section 4.3 (top-k page selection; Gaussian-aware
 selection with the threshold of Appendix C.2 Eq. (18)); the Gaussian page rule
 is this library's reading of the lost Eq. (21)."""
@@ -126,3 +127,60 @@ def test_gauss_select_sizes(MP, alpha):
             assert np.all(row[c:] == -1) and np.all(np.diff(row[:c]) > 0)
             if c == len(want):
                 H.compare_selection(row[:c], want, t, len(want))
+
+
+@pytest.mark.parametrize("MP", [20000, 70000])
+def test_topk_select_one_level_many_rows(MP):
+    """256 (sequence, group) rows: enough rows for one block per row, so the
+    one-level kernels run (keys in registers up to 65536 pages, the
+    global-memory kernel beyond); fewer rows of this length take the
+    two-level chunk + merge path covered above."""
+    print(f"[case] topk one-level MP={MP}", flush=True)
+    B, G, budget = 128, 2, 128
+    lens = [MP * P - (b % 7) * 5 for b in range(B)]
+    rng = np.random.default_rng(MP + 11)
+    score = rng.standard_normal((B, G, MP)).astype(np.float32)
+    score[::3, :, ::50] = 1.5                 # exact ties among high scores
+    sel, cnt, _ = _run_select(_shape(B, G, 1, MP), ekv.SEL_TOPK, lens, 1.5, budget, 3.0,
+                              score=torch.from_numpy(score).cuda())
+    for b in range(0, B, 9):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            U = score[b, g, :M].astype(np.float64)
+            want = oracle.select.topk_pages(U, budget)
+            _check_rows(sel, cnt, b, g, want, U, budget)
+
+
+@pytest.mark.parametrize("MP,theta,lo,hi", [(20000, 0.5, -20, 21), (70000, 995.5, -1000, 1001),
+                                            (9000, 1e9, -5, 5)])
+def test_superset_select_two_level(MP, theta, lo, hi):
+    """Superset rule ([EKV] Appendix B.2) on few long rows (two-level path):
+    integer box scores and a threshold halfway between integers, so the GPU's
+    slightly lowered threshold (it may only add pages) keeps the same pages;
+    the cap ranks by score with ties to the lower page.  Cases: more
+    qualifying pages than the cap, fewer, and none (one page kept)."""
+    print(f"[case] superset MP={MP} theta={theta}", flush=True)
+    B, G, budget, alpha = 2, 3, 200, 1.5
+    lens = [MP * P, MP * P - 17]
+    rng = np.random.default_rng(MP + 5)
+    score = rng.integers(lo, hi, size=(B, G, MP)).astype(np.float32)
+    sh = _shape(B, G, 1, MP)
+    sel = torch.full((B, G, budget), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    tau_lo = torch.full((B, G), theta * (alpha - 1.0), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ekv.select_workspace_bytes(sh, ekv.SEL_SUPERSET, alpha, budget, 3.0), dtype=torch.uint8,
+                     device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ekv.select(sh, ekv.SEL_SUPERSET, sl, alpha, budget, 3.0, torch.from_numpy(score).cuda(), None, None, sel, cnt,
+               tau_lo, ws)
+    H.sync()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            want = oracle.select.superset_pages(score[b, g, :M].astype(np.float64),
+                                                np.array([theta * (alpha - 1.0)]), alpha, budget)
+            c = int(cnt[b, g])
+            assert c == len(want), (b, g, c, len(want))
+            np.testing.assert_array_equal(sel[b, g, :c], want)
+            assert np.all(sel[b, g, c:] == -1)
