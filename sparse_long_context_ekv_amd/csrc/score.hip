@@ -231,9 +231,11 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
 // fp32 statistics (1 KiB per page and group) 256-page blocks, whose staged
 // outputs go out in long runs at the end, beat 16-page blocks by ~3%; with
 // 16-bit statistics (half the bytes per page) the 512 large blocks keep too
-// few loads in flight and 16-page blocks are 25% faster.  Fewer pages when
-// that leaves under 512 blocks for 256 CUs or the block's outputs
-// (`out_per_page` floats per page) would pass 64 KiB of LDS.
+// few loads in flight and 16-page blocks are 25% faster.  Box scores over
+// bf16 min/max on the ragged 64-sequence batch: 64-page blocks 245 us,
+// 16-page 260 us, 256-page 270 us.  Fewer pages when that leaves under 512
+// blocks for 256 CUs or the block's outputs (`out_per_page` floats per page)
+// would pass 64 KiB of LDS.
 static int score_lg_ppb(const Dims& d, int out_per_page, int lg_max) {
     const long units = (long)d.B * d.MP;
     int lg = lg_max;
@@ -258,7 +260,7 @@ static bool allow_64k_lds(K kernel) {
 template <typename T, int D, int R>
 static hipError_t run_box(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
                           const void* kmin, const void* kmax, float* score, hipStream_t s) {
-    int lg = score_lg_ppb(d, d.G, d.kv_bf16 ? 4 : 8);
+    int lg = score_lg_ppb(d, d.G, d.kv_bf16 ? 6 : 8);
     if (((size_t)d.G << lg) * sizeof(float) > 48 * 1024 && !allow_64k_lds(box_score_kernel<T, D, R>)) lg = 2;
     dim3 grid((d.MP + (1 << lg) - 1) >> lg, d.B);
     const size_t lds = ((size_t)d.G << lg) * sizeof(float);
