@@ -1,863 +1,9 @@
-// Sparse alpha-entmax decode over the selected pages ("EntmaxKV:
-// Support-Aware Decoding for Entmax Attention", section 4.1; alpha-entmax of
-// section 2.2; dropped mass of section 3.1).
-//
-//   logits_kernel  grid (page chunks, B*G): gathers each selected page-group
-//                  K tile (16 tokens x D, contiguous) through the page table,
-//                  one token per 16-lane row, and writes s = q.k/sqrt(D) for
-//                  the group's r heads into a [B][HQ][slots] workspace
-//                  (invalid slots -inf).  Per chunk and head it also keeps
-//                  (max, sum exp(s - max), valid count).
-//   tau_kernel     grid (HQ, B): the threshold of sum [x - tau]_+^beta = 1,
-//                  x = (alpha-1) s.  Only x > max(x) - 1 can be in the
-//                  support (the top term alone is at most 1), so those
-//                  candidates are compacted into LDS in slot order; Newton
-//                  steps from tau = max(x) - 1 (where the sum is >= 1) rise
-//                  monotonically to the root because the sum is convex and
-//                  decreasing in tau (beta >= 1); for beta = 1 and 2 the
-//                  closed form on the support found then gives tau exactly
-//                  (beta = 2: tau = m - sqrt((1 - V)/k), m the mean and V the
-//                  centred sum of squares of the k support values).  alpha = 1
-//                  (softmax) takes the log-partition straight from the chunk
-//                  partials.
-//   pv_kernel      grid (slot chunks, B*G): p = [x - tau]_+^beta has exact
-//                  zeros, so only slots with p > 0 for some head of the group
-//                  are compacted and only their V rows are read; partial sums
-//                  need no rescaling.
-//   reduce_kernel  grid (HQ, B): fixed-order sum of the chunk partials.
-// No atomics: every result is bitwise reproducible.
-#include "ekv_device.h"
-#include "ekv_internal.h"
+// Sparse alpha-entmax decode: the workspace plan and the dispatch to the
+// per-dtype kernel launches (decode_bf16.hip, decode_f32.hip); the kernels
+// and what they compute are described in decode_kernels.h.
+#include "decode_kernels.h"
 
 namespace ekv {
-
-enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
-constexpr int kLogitUnroll = 4;
-constexpr int kMaxLogitPpb = 32;       // pages per logits block at most (plan_decode: 8 or 32)
-constexpr int kCandCap = 8192;
-
-// -------------------------------------------------------------- logits ----
-// PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
-// which the general threshold kernel reads (softmax, full cache).
-template <typename T, int D, int R, bool PART>
-__global__ __launch_bounds__(256) void logits_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int lg_ppb,
-    int nslot, int nchunk1, float inv_sqrt_d, float* __restrict__ logits, float* __restrict__ part1) {
-    constexpr int CH = D / kRow;
-    constexpr int NW = Vec<T, CH>::NW;
-    extern __shared__ float stage[];           // [R][ppb * kPage] logits of this chunk
-    __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
-    __shared__ int sh_lp[kMaxLogitPpb], sh_phys[kMaxLogitPpb];
-    const int ppb = 1 << lg_ppb;
-    const int unit = blockIdx.y;
-    const int b = unit / G, g = unit - b * G;
-    const int HQ = G * R;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int i0 = blockIdx.x * ppb;
-    const int i1 = min(cnt, i0 + ppb);
-    const int lane = threadIdx.x & (kRow - 1);
-    const int row = threadIdx.x >> 4;          // token within the page
-
-    Vec<T, CH> qv[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
-
-    float* st = stage + ((lane < R ? lane : 0) << (lg_ppb + 4)) + row;   // lane j < R: head j
-    float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
-    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
-
-    // The chunk's pages: logical index and physical tile, resolved once (one
-    // selection -> page-table chain per block instead of one per page and row).
-    for (int t = threadIdx.x; t < ppb; t += blockDim.x) {
-        const int ii = i0 + t;
-        const int lp = ii < i1 ? (sel ? sel[ii] : ii) : -1;
-        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
-        const bool ok = phys >= 0 && phys < NP;
-        sh_lp[t] = ok ? lp : -1;
-        sh_phys[t] = ok ? phys : -1;
-    }
-    __syncthreads();
-
-    for (int i = i0; i < i1; i += kLogitUnroll) {
-        Vec<T, CH> kv[kLogitUnroll];
-        int lp[kLogitUnroll], phys[kLogitUnroll];
-        bool ok[kLogitUnroll];
-        // Branch-free, so that all loads of the unroll are in flight at once
-        // (a load under a per-page branch waits for the previous ones); an
-        // empty slot reads page 0 and is ignored.
-#pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u) {
-            const int t = min(i + u - i0, ppb - 1);
-            lp[u] = i + u < i1 ? sh_lp[t] : -1;
-            phys[u] = sh_phys[t];
-            ok[u] = lp[u] >= 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u)
-            kv[u].load(k_cache + (((size_t)(ok[u] ? phys[u] : 0) * G + g) * kPage + row) * D + lane * CH);
-#pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u) {
-            const int ii = i + u;
-            if (ii >= i1) break;                       // block-uniform
-            float mine = -INFINITY;
-            if (ok[u]) {                               // block-uniform
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    float acc = 0.0f;
-                    if constexpr (std::is_same<T, float>::value) {
-#pragma unroll
-                        for (int c = 0; c < CH; ++c) acc = fmaf(qv[j].get(c), kv[u].get(c), acc);
-                    } else {
-#pragma unroll
-                        for (int w = 0; w < NW; ++w)
-                            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv[u].w[w]),
-                                                                  __builtin_bit_cast(bf16x2_t, qv[j].w[w]),
-                                                                  acc, false);
-                    }
-                    acc = row_sum16(acc) * inv_sqrt_d;
-                    mine = (lane == j) ? acc : mine;
-                }
-                if (lp[u] * kPage + row >= n) mine = -INFINITY;   // past the sequence end
-            }
-            if (lane < R) {
-                st[(ii - i0) * kPage] = mine;
-                if (PART && mine > -INFINITY) {
-                    if (mine > run_m) {
-                        run_l = run_l * expf(run_m - mine) + 1.0f;
-                        run_m = mine;
-                    } else {
-                        run_l += expf(mine - run_m);
-                    }
-                    run_c += 1.0f;
-                }
-            }
-        }
-    }
-    if (PART && lane < R) {
-        sh_m[row][lane] = run_m;
-        sh_l[row][lane] = run_l;
-        sh_c[row][lane] = run_c;
-    }
-    __syncthreads();
-    // One contiguous run of (i1 - i0) * 16 slots per head.
-    const int nsl = max(i1 - i0, 0) * kPage;
-    const int per_head = ppb * kPage;
-    for (int t = threadIdx.x; t < R * per_head; t += blockDim.x) {
-        const int j = t >> (lg_ppb + 4), r = t & (per_head - 1);
-        if (r < nsl) logits[((size_t)b * HQ + g * R + j) * nslot + i0 * kPage + r] = stage[t];
-    }
-    if (PART && threadIdx.x < R) {
-        const int j = threadIdx.x;
-        float m = -INFINITY;
-        for (int r2 = 0; r2 < kRow; ++r2) m = fmaxf(m, sh_m[r2][j]);
-        float l = 0.0f, c = 0.0f;
-        for (int r2 = 0; r2 < kRow; ++r2) {
-            if (sh_m[r2][j] > -INFINITY) l += sh_l[r2][j] * expf(sh_m[r2][j] - m);
-            c += sh_c[r2][j];
-        }
-        float* o = part1 + (((size_t)b * HQ + g * R + j) * nchunk1 + blockIdx.x) * 3;
-        o[0] = m;
-        o[1] = l;
-        o[2] = c;
-    }
-}
-
-// ----------------------------------------------------------------- tau ----
-struct TauSums {
-    float s1, s0, k;
-};
-
-__device__ __forceinline__ float powb(float d, int mode, float beta) {
-    return mode == kModeBeta1 ? d : (mode == kModeBeta2 ? d * d : powf(d, beta));
-}
-
-__global__ __launch_bounds__(256) void tau_kernel(
-    const float* __restrict__ logits, const float* __restrict__ part1,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
-    int mode, float alpha, float beta, const float* __restrict__ tau_ref, float* __restrict__ tau_out,
-    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
-    __shared__ float cand[kCandCap];
-    __shared__ float red[8];
-    __shared__ int wsum[4];
-    int phase = 0;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int R = HQ / G;
-    const int unit = b * G + h / R;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int nused = cnt * kPage;
-    const size_t oh = (size_t)b * HQ + h;
-
-    // Combine the chunk partials (fixed order).
-    const float* pm = part1 + oh * nchunk1 * 3;
-    float mx = -INFINITY;
-    for (int c = threadIdx.x; c < nchunk1; c += 256) mx = fmaxf(mx, pm[c * 3]);
-    mx = block_max<4>(mx, red, phase);
-    float L = 0.0f, C = 0.0f;
-    for (int c = threadIdx.x; c < nchunk1; c += 256) {
-        const float m = pm[c * 3];
-        if (m > -INFINITY) L += pm[c * 3 + 1] * expf(m - mx);
-        C += pm[c * 3 + 2];
-    }
-    L = block_sum<4>(L, red, phase);
-    C = block_sum<4>(C, red, phase);
-    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
-    if (!(C > 0.0f)) {
-        if (threadIdx.x == 0) {
-            tau_out[oh] = -INFINITY;
-            if (support_out) support_out[oh] = 0;
-            if (delta_out) delta_out[oh] = 1.0f;
-            if (supref_out) supref_out[oh] = 0;
-        }
-        return;
-    }
-    if (mode == kModeSoftmax) {
-        const float lse = mx + logf(L);
-        float kept = 0.0f;
-        if (delta_out) {
-            for (int c = threadIdx.x; c < nchunk1; c += 256) {
-                const float m = pm[c * 3];
-                if (m > -INFINITY) kept += pm[c * 3 + 1] * expf(m - tref);
-            }
-            kept = block_sum<4>(kept, red, phase);
-        }
-        if (threadIdx.x == 0) {
-            tau_out[oh] = lse;
-            if (support_out) support_out[oh] = (int32_t)C;
-            if (delta_out) delta_out[oh] = 1.0f - kept;
-            if (supref_out) supref_out[oh] = (int32_t)C;      // softmax: every token has p > 0
-        }
-        return;
-    }
-
-    const float a = alpha - 1.0f;
-    const float lo = a * mx - 1.0f;
-    const float* lrow = logits + oh * nslot;
-
-    // Candidates x > max(x) - 1, compacted in slot order.
-    int ncand = 0;
-    for (int base = 0; base < nused; base += 256) {
-        const int sl = base + threadIdx.x;
-        const float x = sl < nused ? a * lrow[sl] : -INFINITY;
-        const bool f = x > lo;
-        const uint64_t m = __ballot(f);
-        const int wid = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) == 0) wsum[wid] = __popcll(m);
-        __syncthreads();
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            off += i < wid ? wsum[i] : 0;
-            tot += wsum[i];
-        }
-        const int pos = ncand + off + lanes_below(m);
-        if (f && pos < kCandCap) cand[pos] = x;
-        ncand += tot;
-        __syncthreads();
-    }
-    const bool in_lds = ncand <= kCandCap;
-
-    // Sums over the candidates (LDS), or over every slot with the same filter.
-    auto sums = [&](float t, float t_keep_above, bool want_s0) -> TauSums {
-        float s1 = 0.0f, s0 = 0.0f, k = 0.0f;
-        const int lim = in_lds ? ncand : nused;
-        for (int i = threadIdx.x; i < lim; i += 256) {
-            const float x = in_lds ? cand[i] : a * lrow[i];
-            const float dd = x - t;
-            if (x > t_keep_above && dd > 0.0f) {
-                s1 += powb(dd, mode, beta);
-                if (want_s0) s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? dd : powf(dd, beta - 1.0f));
-                k += 1.0f;
-            }
-        }
-        TauSums r;
-        r.s1 = block_sum<4>(s1, red, phase);
-        r.s0 = want_s0 ? block_sum<4>(s0, red, phase) : 0.0f;
-        r.k = block_sum<4>(k, red, phase);
-        return r;
-    };
-
-    float tau = lo;
-    if (beta >= 1.0f) {
-        for (int it = 0; it < 100; ++it) {
-            const TauSums r = sums(tau, lo, true);
-            const float F = r.s1 - 1.0f;
-            if (!(F > 0.0f) || !(r.s0 > 0.0f)) break;
-            const float nt = tau + F / (beta * r.s0);
-            if (!(nt > tau)) break;
-            tau = nt;
-        }
-    } else {
-        // beta < 1 (alpha > 2): the sum is not convex; bisect.
-        float hi = a * mx - powf(C, 1.0f - alpha);
-        float l2 = lo;
-        for (int it = 0; it < 60; ++it) {
-            const float mid = 0.5f * (l2 + hi);
-            const TauSums r = sums(mid, lo, false);
-            if (r.s1 - 1.0f >= 0.0f) l2 = mid; else hi = mid;
-        }
-        tau = 0.5f * (l2 + hi);
-    }
-
-    // Closed form on the support found (beta = 1 or 2), kept if consistent.
-    if (mode == kModeBeta1 || mode == kModeBeta2) {
-        float sx = 0.0f, k = 0.0f, mn = INFINITY, rest = -INFINITY;
-        const int lim = in_lds ? ncand : nused;
-        for (int i = threadIdx.x; i < lim; i += 256) {
-            const float x = in_lds ? cand[i] : a * lrow[i];
-            if (x > tau) { sx += x; k += 1.0f; mn = fminf(mn, x); }
-            else if (x > lo) rest = fmaxf(rest, x);
-        }
-        sx = block_sum<4>(sx, red, phase);
-        k = block_sum<4>(k, red, phase);
-        mn = -block_max<4>(-mn, red, phase);
-        rest = block_max<4>(rest, red, phase);
-        float tcf = NAN;
-        if (k > 0.0f) {
-            if (mode == kModeBeta1) {
-                tcf = (sx - 1.0f) / k;
-            } else {
-                const float mean = sx / k;
-                float v = 0.0f;
-                for (int i = threadIdx.x; i < lim; i += 256) {
-                    const float x = in_lds ? cand[i] : a * lrow[i];
-                    if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
-                }
-                v = block_sum<4>(v, red, phase);
-                if (v <= 1.0f) tcf = mean - sqrtf((1.0f - v) / k);
-            }
-        }
-        if (tcf == tcf && mn > tcf && !(rest > tcf)) tau = tcf;
-    }
-
-    // Support size and dropped mass with respect to tau_ref.
-    const TauSums fin = sums(tau, lo, false);
-    TauSums ref = {0.0f, 0.0f, 0.0f};
-    if (delta_out || supref_out) ref = sums(tref, lo, false);     // tref >= tau >= lo
-    if (threadIdx.x == 0) {
-        tau_out[oh] = tau;
-        if (support_out) support_out[oh] = (int32_t)fin.k;
-        if (delta_out) delta_out[oh] = 1.0f - ref.s1;
-        if (supref_out) supref_out[oh] = (int32_t)ref.k;
-    }
-}
-
-// ------------------------------------------------------------------ PV ----
-template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void pv_kernel(
-    const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
-    const float* __restrict__ tau, int G, int MP, int NP, int nslot, int spb, int nchunk3, int mode,
-    float alpha, float beta, float* __restrict__ part3) {
-    constexpr int CH = D / kRow;
-    __shared__ int list_slot[256];
-    __shared__ float list_p[256][R];
-    __shared__ int wsum[4];
-    __shared__ float wred[4][R][D];
-    const int unit = blockIdx.y;
-    const int b = unit / G, g = unit - b * G;
-    const int HQ = G * R;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int nused = cnt * kPage;
-    const int s0 = blockIdx.x * spb;
-    const int s1 = min(nused, s0 + spb);
-    const int lane = threadIdx.x & (kRow - 1);
-    const int row = threadIdx.x >> 4;
-    const float a = alpha - 1.0f;
-    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
-
-    float tj[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) tj[j] = tau[(size_t)b * HQ + g * R + j];
-
-    float acc[R][CH];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int c = 0; c < CH; ++c) acc[j][c] = 0.0f;
-
-    for (int base = s0; base < s1; base += 256) {
-        const int sl = base + threadIdx.x;
-        float pj[R];
-        bool any = false;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            float p = 0.0f;
-            if (sl < s1 && tj[j] > -INFINITY) {
-                const float s = logits[((size_t)b * HQ + g * R + j) * nslot + sl];
-                if (mode == kModeSoftmax) {
-                    p = s > -INFINITY ? expf(s - tj[j]) : 0.0f;
-                } else {
-                    const float dd = a * s - tj[j];
-                    p = dd > 0.0f ? powb(dd, mode, beta) : 0.0f;
-                }
-            }
-            pj[j] = p;
-            any = any || p > 0.0f;
-        }
-        const uint64_t m = __ballot(any);
-        const int wid = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) == 0) wsum[wid] = __popcll(m);
-        __syncthreads();
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            off += i < wid ? wsum[i] : 0;
-            tot += wsum[i];
-        }
-        if (any) {
-            const int pos = off + lanes_below(m);
-            list_slot[pos] = sl;
-#pragma unroll
-            for (int j = 0; j < R; ++j) list_p[pos][j] = pj[j];
-        }
-        __syncthreads();
-        for (int e = row; e < tot; e += kRow) {
-            const int slot = list_slot[e];
-            const int ip = slot >> 4, t = slot & (kPage - 1);
-            const int lp = sel ? sel[ip] : ip;
-            if (lp < 0 || lp >= M) continue;
-            const int phys = page_table[(size_t)b * MP + lp];
-            if (phys < 0 || phys >= NP) continue;
-            Vec<T, CH> vv;
-            vv.load(v_cache + (((size_t)phys * G + g) * kPage + t) * D + lane * CH);
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const float p = list_p[e][j];
-#pragma unroll
-                for (int c = 0; c < CH; ++c) acc[j][c] = fmaf(p, vv.get(c), acc[j][c]);
-            }
-        }
-        __syncthreads();
-    }
-
-    // Reduce the 16 rows: rows of a wave by cross-lane adds (fixed order),
-    // then the 4 waves through LDS.
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            float v = acc[j][c];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[j][c] = v;
-        }
-    const int wid = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) < kRow) {
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-#pragma unroll
-            for (int c = 0; c < CH; ++c) wred[wid][j][lane * CH + c] = acc[j][c];
-    }
-    __syncthreads();
-    for (int o = threadIdx.x; o < R * D; o += 256) {
-        const int j = o / D, c = o - j * D;
-        const float v = ((wred[0][j][c] + wred[1][j][c]) + wred[2][j][c]) + wred[3][j][c];
-        part3[(((size_t)b * HQ + g * R + j) * nchunk3 + blockIdx.x) * D + c] = v;
-    }
-}
-
-__global__ void reduce_kernel(const float* __restrict__ part3, int HQ, int D, int nchunk3,
-                              float* __restrict__ out) {
-    const int h = blockIdx.x, b = blockIdx.y;
-    const size_t oh = (size_t)b * HQ + h;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-        float s = 0.0f;
-        for (int k = 0; k < nchunk3; ++k) s += part3[(oh * nchunk3 + k) * D + c];
-        out[oh * D + c] = s;
-    }
-}
-
-// ------------------------------------------------- fused tau + PV (sparse) ----
-constexpr int kFusedMaxSlots = 4096;   // selected slots per head on the fused path
-constexpr int kCandLds = 1024;         // threshold candidates per head kept in LDS
-constexpr int kPvList = 512;           // support entries per PV pass
-
-// Orders this wave's LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int MODE>
-__device__ __forceinline__ float pw(float d, float beta) {      // d^beta, d > 0
-    return MODE == kModeBeta1 ? d : (MODE == kModeBeta2 ? d * d : powf(d, beta));
-}
-template <int MODE>
-__device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d > 0
-    return MODE == kModeBeta1 ? 1.0f : (MODE == kModeBeta2 ? d : powf(d, beta - 1.0f));
-}
-
-// One block per (sequence, KV group): the r query heads of the group, each
-// split over W waves (W = 16 / r, at most the register chunks available), so
-// a wave holds KPLW float4 of logits per lane; slot k*256 + 4*lane + c of the
-// wave's part sits in xr[k][c], invalid slots -inf.  Per head:
-//  0. the block stages the physical page of every selected page in LDS (its
-//     loads overlap the logits loads);
-//  1. max(x) over the head's waves (x = (alpha-1) s);
-//  2. each wave compacts its threshold candidates x > max(x) - 1 (only those
-//     can be in the support: the top term alone is at most 1) with their
-//     slots into its own LDS list, lane by lane after one wave scan of
-//     per-lane counts (a fixed order, so results are reproducible); past CW
-//     candidates the wave keeps working on its registers;
-//  3. tau from sum [x - tau]_+^beta = 1 by Newton steps on F^(1/beta) from
-//     tau = max(x) - 1: for beta >= 1 this is the L^beta norm of (x - tau)_+,
-//     convex and decreasing, so the steps rise monotonically without passing
-//     the root (beta < 1: bisection).  Each iteration sums per wave, and the
-//     head's W partials are added in a fixed order after one block barrier
-//     (partials double-buffered); for beta in {1, 2} the closed form on the
-//     support found then gives tau exactly;
-//  4. tau, the support size and the dropped mass w.r.t. tau_ref (tau_ref,
-//     the threshold over a superset of these tokens, is at least max(x) - 1,
-//     so only candidates contribute);
-//  5. each wave compacts its part of the support (slot, p = [x - tau]_+^beta)
-//     and gathers only those V rows, four per step across the 16-lane rows;
-//     the W partial outputs are summed in a fixed order.
-template <typename T, int D, int R, int W, int KPLW, int MODE>
-__global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
-    const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
-    int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
-    float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
-    float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
-    constexpr int NWV = R * W;                   // waves in the block
-    constexpr int CH = D / kRow;
-    constexpr int PVU = 4;                       // V rows per 16-lane row in flight
-    constexpr int NPG = W * KPLW * 256 / kPage;  // selected pages per head at most
-    constexpr int CW = kCandLds / W;             // candidates per wave kept in LDS
-    constexpr int PW = kPvList / W;              // support entries per wave per pass
-    __shared__ float cand_x[NWV][CW + 64];       // + one dump slot per lane
-    __shared__ int cand_s[NWV][CW + 64];
-    __shared__ int pv_slot[NWV][PW + 64];
-    __shared__ float pv_p[NWV][PW + 64];
-    __shared__ int phys_of[NPG];
-    __shared__ float part[2][NWV][4];
-    __shared__ int flag[2][NWV];
-    __shared__ float pvout[NWV][D];
-    const int unit = blockIdx.x;
-    const int b = unit / G, g = unit - b * G;
-    const int HQ = G * R;
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int j = wv / W, w = wv - j * W;
-    const size_t oh = (size_t)b * HQ + g * R + j;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = min(max(sel_count[unit], 0), min(sel_stride, NPG));
-    const int nused = cnt * kPage;
-    const size_t nslot = (size_t)sel_stride * kPage;
-    const float a = alpha - 1.0f;
-    const int base = w * KPLW * 256;             // first slot of this wave's part
-    const float* lrow = logits + oh * nslot;
-    float* o = out + oh * D;
-
-    // 0. selected logical pages -> physical pages (loads first), then the logits
-    const int32_t* sel = sel_pages + (size_t)unit * sel_stride;
-    const int32_t* pt = page_table + (size_t)b * MP;
-    constexpr int NPL = (NPG + 64 * NWV - 1) / (64 * NWV);
-    int lpg[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int ip = i * 64 * NWV + (int)threadIdx.x;
-        lpg[i] = ip < cnt ? sel[ip] : -1;
-    }
-    float xr[KPLW][4];
-#pragma unroll
-    for (int k = 0; k < KPLW; ++k) {
-        const int s0 = base + k * 256 + 4 * lane;
-        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (s0 < nused) v = *reinterpret_cast<const float4*>(lrow + s0);
-        xr[k][0] = v.x;
-        xr[k][1] = v.y;
-        xr[k][2] = v.z;
-        xr[k][3] = v.w;
-    }
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int ip = i * 64 * NWV + (int)threadIdx.x;
-        if (ip < NPG) {
-            const int lp = lpg[i];
-            const int ph = (lp >= 0 && lp < M) ? pt[lp] : -1;
-            phys_of[ip] = (ph >= 0 && ph < NP) ? ph : -1;
-        }
-    }
-
-    // 1. max over the head (and the valid count, for the bisection bracket)
-    float xm = -INFINITY;
-    int nv = 0;
-#pragma unroll
-    for (int k = 0; k < KPLW; ++k)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            xr[k][c] *= a;
-            xm = fmaxf(xm, xr[k][c]);
-            nv += xr[k][c] > -INFINITY ? 1 : 0;
-        }
-    xm = wave_max(xm);
-    nv = wave_isum(nv);
-    if (lane == 0) {
-        part[0][wv][0] = xm;
-        part[0][wv][1] = (float)nv;
-    }
-    __syncthreads();
-    float xmax = -INFINITY, nvalid = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) {
-        xmax = fmaxf(xmax, part[0][j * W + w2][0]);
-        nvalid += part[0][j * W + w2][1];
-    }
-    // A head without a finite logit (no valid slot, or non-finite inputs) does
-    // no work but still takes part in every barrier below.
-    const bool empty = !(xmax > -INFINITY);
-    const float lo = empty ? 0.0f : xmax - 1.0f;
-
-    // 2. this wave's candidates x > lo
-    int mine = 0;
-#pragma unroll
-    for (int k = 0; k < KPLW; ++k)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mine += xr[k][c] > lo ? 1 : 0;
-    const int incl = wave_incl_scan(mine);
-    const int ncand = __builtin_amdgcn_readlane(incl, 63);
-    const bool in_lds = ncand <= CW;
-    float* cx = cand_x[wv];
-    int* cs = cand_s[wv];
-    if (in_lds) {
-        int pos = incl - mine;
-        const int dump = CW + lane;
-#pragma unroll
-        for (int k = 0; k < KPLW; ++k)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool f = xr[k][c] > lo;
-                const int at = f ? pos : dump;
-                cx[at] = xr[k][c];
-                cs[at] = base + k * 256 + 4 * lane + c;
-                pos += f ? 1 : 0;
-            }
-        wave_lds_sync();
-    }
-    auto each_cand = [&](auto&& fn) {
-        if (in_lds) {
-            for (int i = lane; i < ncand; i += 64) fn(cx[i], cs[i]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < KPLW; ++k)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (xr[k][c] > lo) fn(xr[k][c], base + k * 256 + 4 * lane + c);
-        }
-    };
-    // Sum of the head's W wave partials (fixed order), after a barrier.
-    int pb = 1;
-    auto head_sums = [&](float v0, float v1, float v2, float v3, int fl, float* r, bool& any) {
-        pb ^= 1;
-        if (lane == 0) {
-            part[pb][wv][0] = v0;
-            part[pb][wv][1] = v1;
-            part[pb][wv][2] = v2;
-            part[pb][wv][3] = v3;
-            flag[pb][wv] = fl;
-        }
-        __syncthreads();
-        r[0] = r[1] = r[2] = r[3] = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < W; ++w2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] += part[pb][j * W + w2][i];
-        any = false;
-#pragma unroll
-        for (int v2 = 0; v2 < NWV; ++v2) any = any || flag[pb][v2] != 0;
-    };
-
-    // 3. tau
-    float tau = lo;
-    if (MODE != kModeGeneral || beta >= 1.0f) {
-        bool active = !empty;
-        for (int it = 0; it < 100; ++it) {
-            float s1 = 0.0f, s0 = 0.0f;
-            if (active)
-                each_cand([&](float x, int) {
-                    const float d = x - tau;
-                    if (d > 0.0f) {
-                        s1 += pw<MODE>(d, beta);
-                        s0 += pw1<MODE>(d, beta);
-                    }
-                });
-            s1 = wave_sum(s1);
-            s0 = wave_sum(s0);
-            float r[4];
-            bool any;
-            head_sums(s1, s0, 0.0f, 0.0f, active ? 1 : 0, r, any);
-            if (!any) break;                                 // block-uniform
-            if (active) {
-                const float f = r[0], df = r[1];
-                if (!(f > 1.0f) || !(df > 0.0f)) {
-                    active = false;
-                } else {
-                    const float gr = MODE == kModeBeta1 ? f : (MODE == kModeBeta2 ? sqrtf(f) : powf(f, 1.0f / beta));
-                    const float nt = tau + (1.0f - 1.0f / gr) * f / df;
-                    if (!(nt > tau)) active = false; else tau = nt;
-                }
-            }
-        }
-    } else {
-        // beta < 1 (alpha > 2): bisection on [max - 1, max - n^(1-alpha)]
-        float l2 = lo, hi = xmax - powf(nvalid, 1.0f - alpha);
-        for (int it = 0; it < 60; ++it) {
-            const float mid = 0.5f * (l2 + hi);
-            float s1 = 0.0f;
-            each_cand([&](float x, int) {
-                const float d = x - mid;
-                if (d > 0.0f) s1 += pw<MODE>(d, beta);
-            });
-            s1 = wave_sum(s1);
-            float r[4];
-            bool any;
-            head_sums(s1, 0.0f, 0.0f, 0.0f, 0, r, any);
-            if (r[0] >= 1.0f) l2 = mid; else hi = mid;
-        }
-        tau = 0.5f * (l2 + hi);
-    }
-    // Closed form on the support found (beta in {1, 2}), kept if consistent.
-    if constexpr (MODE == kModeBeta1 || MODE == kModeBeta2) {
-        float sx = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
-        each_cand([&](float x, int) {
-            if (x > tau) { sx += x; kk += 1.0f; mn = fminf(mn, x); }
-            else rest = fmaxf(rest, x);
-        });
-        float r[4];
-        bool any;
-        head_sums(wave_sum(sx), wave_sum(kk), -wave_max(-mn), wave_max(rest), 0, r, any);
-        // r[2], r[3] (sums) are unused: the min and the max are taken over the waves
-        float mnh = INFINITY, resth = -INFINITY;
-#pragma unroll
-        for (int w2 = 0; w2 < W; ++w2) {
-            mnh = fminf(mnh, part[pb][j * W + w2][2]);
-            resth = fmaxf(resth, part[pb][j * W + w2][3]);
-        }
-        const float sxh = r[0], kkh = r[1];
-        float tcf = NAN;
-        if constexpr (MODE == kModeBeta1) {
-            if (kkh > 0.0f) tcf = (sxh - 1.0f) / kkh;
-        } else {
-            const float mean = kkh > 0.0f ? sxh / kkh : 0.0f;
-            float v = 0.0f;
-            each_cand([&](float x, int) {
-                if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
-            });
-            head_sums(wave_sum(v), 0.0f, 0.0f, 0.0f, 0, r, any);
-            if (kkh > 0.0f && r[0] <= 1.0f) tcf = mean - sqrtf((1.0f - r[0]) / kkh);
-        }
-        if (tcf == tcf && mnh > tcf && !(resth > tcf)) tau = tcf;
-    }
-
-    // 4. support size and dropped mass with respect to tau_ref
-    // (every token above tau_ref is a candidate: tau_ref >= tau >= max - 1)
-    int ns = 0, nref = 0;
-    float kept = 0.0f;
-    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
-    const bool want_ref = delta_out || supref_out;
-    if (!empty) each_cand([&](float x, int) {
-        ns += x > tau ? 1 : 0;
-        if (want_ref && x > tref) {
-            kept += pw<MODE>(x - tref, beta);
-            ++nref;
-        }
-    });
-    const int sinc = wave_incl_scan(ns);
-    const int nsw = __builtin_amdgcn_readlane(sinc, 63);      // this wave's support
-    {
-        float r[4];
-        bool any;
-        head_sums((float)nsw, want_ref ? wave_sum(kept) : 0.0f, want_ref ? (float)wave_isum(nref) : 0.0f, 0.0f, 0,
-                  r, any);
-        if (w == 0 && lane == 0) {
-            tau_out[oh] = empty ? -INFINITY : tau;
-            if (support_out) support_out[oh] = empty ? 0 : (int32_t)r[0];
-            if (delta_out) delta_out[oh] = empty ? 1.0f : 1.0f - r[1];
-            if (supref_out) supref_out[oh] = empty ? 0 : (int32_t)r[2];
-        }
-    }
-
-    // 5. PV over this wave's part of the support, in passes of PW entries.
-    const int rg = lane >> 4, l16 = lane & (kRow - 1);
-    int* ls = pv_slot[wv];
-    float* lpv = pv_p[wv];
-    float acc[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
-    for (int start = 0; start < nsw; start += PW) {
-        if (start > 0) wave_lds_sync();          // the previous pass has read its list
-        int pos = sinc - ns - start;
-        const int dump = PW + lane;
-        each_cand([&](float x, int slot) {
-            if (x > tau) {
-                const int at = (pos >= 0 && pos < PW) ? pos : dump;
-                ls[at] = slot;
-                lpv[at] = pw<MODE>(x - tau, beta);
-                ++pos;
-            }
-        });
-        wave_lds_sync();
-        const int nent = min(nsw - start, PW);
-        for (int e0 = 0; e0 < nent; e0 += 4 * PVU) {
-            Vec<T, CH> vv[PVU];
-            float pp[PVU];
-            bool okv[PVU];
-            // Branch-free, so that the PVU row loads are in flight together
-            // (a load under a branch waits for the earlier ones); a slot past
-            // the list reads entry 0's row of page 0 and is ignored.
-#pragma unroll
-            for (int u = 0; u < PVU; ++u) {
-                const int e = e0 + 4 * u + rg;
-                const int ec = e < nent ? e : 0;
-                const int slot = ls[ec];
-                const int phys = phys_of[slot >> 4];
-                okv[u] = e < nent && phys >= 0;
-                pp[u] = okv[u] ? lpv[ec] : 0.0f;
-                vv[u].load(v_cache + (((size_t)(okv[u] ? phys : 0) * G + g) * kPage + (slot & (kPage - 1))) * D +
-                           l16 * CH);
-            }
-#pragma unroll
-            for (int u = 0; u < PVU; ++u)
-                if (okv[u])
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) acc[c] = fmaf(pp[u], vv[u].get(c), acc[c]);
-        }
-    }
-    // Fixed-order sums: the four 16-lane rows of the wave, then the head's waves.
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        float v = acc[c];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        acc[c] = v;
-    }
-    if (lane < kRow) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) pvout[wv][l16 * CH + c] = acc[c];
-    }
-    __syncthreads();
-    if (w == 0) {
-        for (int c = lane; c < D; c += 64) {
-            float v = 0.0f;
-#pragma unroll
-            for (int w2 = 0; w2 < W; ++w2) v += pvout[j * W + w2][c];
-            o[c] = v;
-        }
-    }
-}
 
 // ---------------------------------------------------------------- host ----
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -888,80 +34,6 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     return pl;
 }
 
-template <typename T, int D, int R, int MODE>
-static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_cache, const int32_t* pt,
-                            const int32_t* sl, const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                            float alpha, float beta, const float* logits, const float* tau_ref, float* out,
-                            float* tau, int32_t* support, float* delta, int32_t* supref, hipStream_t s) {
-    const int units = d.B * d.G;
-    // KPL float4 of logits per lane in all; W = 16 / R waves per head, at most KPL.
-    constexpr int WMAX = 16 / R;
-#define EKV_FUSED(KPL)                                                                                      \
-    {                                                                                                       \
-        constexpr int W = WMAX < KPL ? WMAX : KPL;                                                          \
-        sparse_tau_pv_kernel<T, D, R, W, KPL / W, MODE><<<dim3(units), dim3(64 * R * W), 0, s>>>(           \
-            (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
-            tau_ref, out, tau, support, delta, supref);                                                     \
-        return hipGetLastError();                                                                           \
-    }
-    if (pl.nslot <= 256) EKV_FUSED(1)
-    if (pl.nslot <= 512) EKV_FUSED(2)
-    if (pl.nslot <= 1024) EKV_FUSED(4)
-    if (pl.nslot <= 2048) EKV_FUSED(8)
-    EKV_FUSED(16)
-#undef EKV_FUSED
-}
-
-template <typename T, int D, int R>
-static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* pt, const int32_t* sl,
-                             const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                             float alpha, int mode, float beta, const float* tau_ref, float* out,
-                             float* tau, int32_t* support, float* delta, int32_t* supref, char* ws,
-                             hipStream_t s) {
-    float* logits = (float*)(ws + pl.off_logits);
-    float* part1 = (float*)(ws + pl.off_part1);
-    float* part3 = (float*)(ws + pl.off_part3);
-    const int units = d.B * d.G;
-    const size_t lds = ((size_t)R * pl.ppb * kPage) * sizeof(float);
-    if (pl.fused) {
-        logits_kernel<T, D, R, false><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
-            (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
-            pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        switch (mode) {
-            case kModeBeta1:
-                return run_fused<T, D, R, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
-            case kModeBeta2:
-                return run_fused<T, D, R, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
-            default:
-                return run_fused<T, D, R, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,
-                                                        sel_stride, alpha, beta, logits, tau_ref, out, tau,
-                                                        support, delta, supref, s);
-        }
-    }
-    logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
-        (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
-        pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
-                                                     d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
-                                                     tau_ref, tau, support, delta, supref);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(
-        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, tau, d.G, d.MP, d.NP,
-        pl.nslot, pl.spb, pl.nchunk3, mode, alpha, beta, part3);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    reduce_kernel<<<dim3(d.HQ, d.B), dim3(D), 0, s>>>(part3, d.HQ, D, pl.nchunk3, out);
-    return hipGetLastError();
-}
-
 hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
@@ -975,25 +47,9 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
         beta = 1.0f / (alpha - 1.0f);
         mode = (beta == 1.0f) ? kModeBeta1 : (beta == 2.0f ? kModeBeta2 : kModeGeneral);
     }
-#define EKV_DEC(RR, T, DD)                                                                       \
-    return run_decode<T, DD, RR>(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages,    \
-                                 sel_count, sel_stride, alpha, mode, beta, tau_ref, out, tau,     \
-                                 support, delta, supref, ws, s)
-#define EKV_RSW(T, DD)                          \
-    switch (d.R) {                              \
-        case 1: EKV_DEC(1, T, DD);              \
-        case 2: EKV_DEC(2, T, DD);              \
-        case 4: EKV_DEC(4, T, DD);              \
-        case 8: EKV_DEC(8, T, DD);              \
-        default: return hipErrorInvalidValue;   \
-    }
-    if (d.kv_bf16) {
-        if (d.D == 128) { EKV_RSW(bf16_t, 128) } else { EKV_RSW(bf16_t, 64) }
-    } else {
-        if (d.D == 128) { EKV_RSW(float, 128) } else { EKV_RSW(float, 64) }
-    }
-#undef EKV_RSW
-#undef EKV_DEC
+    return (d.kv_bf16 ? launch_decode_bf16 : launch_decode_f32)(d, pl, q, k_cache, v_cache, page_table, seq_lens,
+                                                               sel_pages, sel_count, sel_stride, alpha, mode, beta,
+                                                               tau_ref, out, tau, support, delta, supref, ws, s);
 }
 
 }  // namespace ekv

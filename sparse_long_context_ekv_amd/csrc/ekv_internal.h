@@ -64,4 +64,18 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
                          float alpha, const float* tau_ref, float* out, float* tau,
                          int32_t* support, float* delta, int32_t* supref, char* ws, hipStream_t s);
 
+// Per-dtype decode launches (decode_bf16.hip, decode_f32.hip); mode is the
+// entmax mode of decode_kernels.h and beta = 1/(alpha-1).
+hipError_t launch_decode_bf16(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
+                         int mode, float beta, const float* tau_ref, float* out, float* tau, int32_t* support,
+                         float* delta, int32_t* supref, char* ws, hipStream_t s);
+hipError_t launch_decode_f32(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
+                         int mode, float beta, const float* tau_ref, float* out, float* tau, int32_t* support,
+                         float* delta, int32_t* supref, char* ws, hipStream_t s);
+
+
 }  // namespace ekv
