@@ -485,7 +485,6 @@ static __global__ void reduce_kernel(const float* __restrict__ part3, int HQ, in
 // ------------------------------------------------- fused tau + PV (sparse) ----
 constexpr int kFusedMaxSlots = 4096;   // selected slots per head on the fused path
 constexpr int kCandLds = 1024;         // threshold candidates per head kept in LDS
-constexpr int kFusedBlocks = 256;      // split a group's heads over blocks up to this many blocks (one per CU)
 constexpr int kPvList = 512;           // support entries per PV pass
 
 // Orders this wave's LDS writes before its later LDS reads.
@@ -504,13 +503,10 @@ __device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d
     return MODE == kModeBeta1 ? 1.0f : (MODE == kModeBeta2 ? d : powf(d, beta - 1.0f));
 }
 
-// One block per (sequence, KV group) and part of its heads: RB of the
-// group's r query heads (RB = r, or fewer when there are fewer (sequence,
-// group) units than compute units, so that the heads of a unit run in
-// several blocks), each split over W waves (W = 16 / RB, at most the
-// register chunks available), so a wave holds KPLW float4 of logits per
-// lane; slot k*256 + 4*lane + c of the wave's part sits in xr[k][c],
-// invalid slots -inf.  Per head:
+// One block per (sequence, KV group): the r query heads of the group, each
+// split over W waves (W = 16 / r, at most the register chunks available), so
+// a wave holds KPLW float4 of logits per lane; slot k*256 + 4*lane + c of the
+// wave's part sits in xr[k][c], invalid slots -inf.  Per head:
 //  0. the block stages the physical page of every selected page in LDS (its
 //     loads overlap the logits loads);
 //  1. max(x) over the head's waves (x = (alpha-1) s);
@@ -532,15 +528,15 @@ __device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d
 //  5. each wave compacts its part of the support (slot, p = [x - tau]_+^beta)
 //     and gathers only those V rows, four per step across the 16-lane rows;
 //     the W partial outputs are summed in a fixed order.
-template <typename T, int D, int R, int RB, int W, int KPLW, int MODE>
-__global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
+template <typename T, int D, int R, int W, int KPLW, int MODE>
+__global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
     int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
     float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
     float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
-    constexpr int NWV = RB * W;                  // waves in the block
+    constexpr int NWV = R * W;                   // waves in the block
     constexpr int CH = D / kRow;
     constexpr int PVU = 4;                       // V rows per 16-lane row in flight
     constexpr int NPG = W * KPLW * 256 / kPage;  // selected pages per head at most
@@ -554,13 +550,12 @@ __global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
     __shared__ float part[2][NWV][4];
     __shared__ int flag[2][NWV];
     __shared__ float pvout[NWV][D];
-    constexpr int NSPLIT = R / RB;               // blocks per (sequence, group)
-    const int unit = blockIdx.x / NSPLIT, hpart = blockIdx.x - unit * NSPLIT;
+    const int unit = blockIdx.x;
     const int b = unit / G, g = unit - b * G;
     const int HQ = G * R;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int jl = wv / W, w = wv - jl * W;      // head within the block, wave within the head
-    const size_t oh = (size_t)b * HQ + g * R + hpart * RB + jl;
+    const int j = wv / W, w = wv - j * W;
+    const size_t oh = (size_t)b * HQ + g * R + j;
     const int n = seq_len_at(seq_lens, b, MP);
     const int M = num_pages(n);
     const int cnt = min(max(sel_count[unit], 0), min(sel_stride, NPG));
@@ -623,8 +618,8 @@ __global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
     float xmax = -INFINITY, nvalid = 0.0f;
 #pragma unroll
     for (int w2 = 0; w2 < W; ++w2) {
-        xmax = fmaxf(xmax, part[0][jl * W + w2][0]);
-        nvalid += part[0][jl * W + w2][1];
+        xmax = fmaxf(xmax, part[0][j * W + w2][0]);
+        nvalid += part[0][j * W + w2][1];
     }
     // A head without a finite logit (no valid slot, or non-finite inputs) does
     // no work but still takes part in every barrier below.
@@ -684,7 +679,7 @@ __global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
 #pragma unroll
         for (int w2 = 0; w2 < W; ++w2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] += part[pb][jl * W + w2][i];
+            for (int i = 0; i < 4; ++i) r[i] += part[pb][j * W + w2][i];
         any = false;
 #pragma unroll
         for (int v2 = 0; v2 < NWV; ++v2) any = any || flag[pb][v2] != 0;
@@ -753,8 +748,8 @@ __global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
         float mnh = INFINITY, resth = -INFINITY;
 #pragma unroll
         for (int w2 = 0; w2 < W; ++w2) {
-            mnh = fminf(mnh, part[pb][jl * W + w2][2]);
-            resth = fmaxf(resth, part[pb][jl * W + w2][3]);
+            mnh = fminf(mnh, part[pb][j * W + w2][2]);
+            resth = fmaxf(resth, part[pb][j * W + w2][3]);
         }
         const float sxh = r[0], kkh = r[1];
         float tcf = NAN;
@@ -863,24 +858,24 @@ __global__ __launch_bounds__(64 * RB * W) void sparse_tau_pv_kernel(
         for (int c = lane; c < D; c += 64) {
             float v = 0.0f;
 #pragma unroll
-            for (int w2 = 0; w2 < W; ++w2) v += pvout[jl * W + w2][c];
+            for (int w2 = 0; w2 < W; ++w2) v += pvout[j * W + w2][c];
             o[c] = v;
         }
     }
 }
 
-template <typename T, int D, int R, int RB, int MODE>
+template <typename T, int D, int R, int MODE>
 static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_cache, const int32_t* pt,
                             const int32_t* sl, const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
                             float alpha, float beta, const float* logits, const float* tau_ref, float* out,
                             float* tau, int32_t* support, float* delta, int32_t* supref, hipStream_t s) {
     const int units = d.B * d.G;
-    // KPL float4 of logits per lane in all; W = 16 / RB waves per head, at most KPL.
-    constexpr int WMAX = 16 / RB;
+    // KPL float4 of logits per lane in all; W = 16 / R waves per head, at most KPL.
+    constexpr int WMAX = 16 / R;
 #define EKV_FUSED(KPL)                                                                                      \
     {                                                                                                       \
         constexpr int W = WMAX < KPL ? WMAX : KPL;                                                          \
-        sparse_tau_pv_kernel<T, D, R, RB, W, KPL / W, MODE><<<dim3(units * (R / RB)), dim3(64 * RB * W), 0, s>>>( \
+        sparse_tau_pv_kernel<T, D, R, W, KPL / W, MODE><<<dim3(units), dim3(64 * R * W), 0, s>>>(           \
             (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
             tau_ref, out, tau, support, delta, supref);                                                     \
         return hipGetLastError();                                                                           \
@@ -911,30 +906,18 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
             pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // Heads per block: all r of the group, or r/4 (at least 1) when that
-        // still leaves at most kFusedBlocks blocks (one per compute unit):
-        // with few (sequence, group) units, more waves per head shorten the
-        // threshold and PV loops (1M tokens, 8 units: 13.6 -> ~9 us).
-        constexpr int RS = R >= 4 ? R / 4 : 1;
-        const bool split = RS < R && (long)units * (R / RS) <= kFusedBlocks;
-#define EKV_FMODE(RBV)                                                                                        \
-        switch (mode) {                                                                                       \
-            case kModeBeta1:                                                                                  \
-                return run_fused<T, D, R, RBV, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count,       \
-                                                           sel_stride, alpha, beta, logits, tau_ref, out, tau, \
-                                                           support, delta, supref, s);                        \
-            case kModeBeta2:                                                                                  \
-                return run_fused<T, D, R, RBV, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count,       \
-                                                           sel_stride, alpha, beta, logits, tau_ref, out, tau, \
-                                                           support, delta, supref, s);                        \
-            default:                                                                                          \
-                return run_fused<T, D, R, RBV, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,     \
-                                                             sel_stride, alpha, beta, logits, tau_ref, out,    \
-                                                             tau, support, delta, supref, s);                 \
+        switch (mode) {
+            case kModeBeta1:
+                return run_fused<T, D, R, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
+            case kModeBeta2:
+                return run_fused<T, D, R, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
+                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
+            default:
+                return run_fused<T, D, R, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,
+                                                        sel_stride, alpha, beta, logits, tau_ref, out, tau,
+                                                        support, delta, supref, s);
         }
-        if constexpr (RS < R) { if (split) { EKV_FMODE(RS) } }
-        EKV_FMODE(R)
-#undef EKV_FMODE
     }
     logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
         (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
