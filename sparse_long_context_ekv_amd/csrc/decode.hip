@@ -24,12 +24,23 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     const size_t bh = (size_t)d.B * d.HQ;
     pl.off_logits = 0;
     pl.off_part1 = align256(bh * pl.nslot * sizeof(float));
+    pl.ncc = 0;
+    pl.off_cand = pl.off_ccnt = 0;
     if (pl.fused) {
         pl.off_part3 = pl.off_part1;
         pl.bytes = pl.off_part1;
     } else {
         pl.off_part3 = pl.off_part1 + align256(bh * pl.nchunk1 * 3 * sizeof(float));
         pl.bytes = pl.off_part3 + align256(bh * pl.nchunk3 * d.D * sizeof(float));
+        // Entmax over many slots: the threshold candidates are compacted by
+        // many blocks (cand_kernel) instead of inside the one block per head.
+        const int ncc = (pl.nslot + kCandChunk - 1) / kCandChunk;
+        if (alpha > 1.0f && ncc >= 2 && ncc <= kCandMaxChunks) {
+            pl.ncc = ncc;
+            pl.off_cand = pl.bytes;
+            pl.off_ccnt = pl.off_cand + align256(bh * ncc * kCandPerChunk * sizeof(float));
+            pl.bytes = pl.off_ccnt + align256(bh * ncc * sizeof(int));
+        }
     }
     return pl;
 }

@@ -39,7 +39,10 @@ namespace ekv {
 enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
 constexpr int kLogitUnroll = 4;
 constexpr int kMaxLogitPpb = 32;       // pages per logits block at most (plan_decode: 8 or 32)
-constexpr int kCandCap = 8192;
+constexpr int kCandCap = 8192;        // threshold candidates per head kept in LDS (general path)
+constexpr int kCandChunk = 4096;      // slots per cand_kernel block (256 threads x 16)
+constexpr int kCandPerChunk = 1024;   // candidates a chunk may hand over; more: the chunk overflows
+constexpr int kCandMaxChunks = 1024;  // chunks per head at most on the cand_kernel path
 
 // -------------------------------------------------------------- logits ----
 // PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
@@ -185,10 +188,12 @@ static __global__ __launch_bounds__(256) void tau_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
     int mode, float alpha, float beta, const float* __restrict__ tau_ref, float* __restrict__ tau_out,
-    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
+    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out,
+    const float* __restrict__ ccand, const int32_t* __restrict__ ccnt, int ncc) {
     __shared__ float cand[kCandCap];
+    __shared__ int coff[kCandMaxChunks + 1];
     __shared__ float red[8];
-    __shared__ int wsum[4];
+    __shared__ int wsum[8];
     int phase = 0;
     const int h = blockIdx.x, b = blockIdx.y;
     const int R = HQ / G;
@@ -245,9 +250,49 @@ static __global__ __launch_bounds__(256) void tau_kernel(
     const float lo = a * mx - 1.0f;
     const float* lrow = logits + oh * nslot;
 
-    // Candidates x > max(x) - 1, compacted in slot order.
+    // Candidates x > max(x) - 1, compacted in slot order: gathered from
+    // cand_kernel's per-chunk lists when it ran and no chunk overflowed (the
+    // same values in the same order), else by this block.
     int ncand = 0;
-    for (int base = 0; base < nused; base += 256) {
+    bool gathered = false;
+    if (ccand) {
+        const int32_t* cc = ccnt + oh * ncc;
+        int mine[4], sum = 0;
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * (int)threadIdx.x + i;
+            mine[i] = c < ncc ? cc[c] : 0;
+            over = over || mine[i] < 0;
+            sum += mine[i] > 0 ? mine[i] : 0;
+        }
+        int ex, ex2, tot, tot2;
+        block_excl_scan2<4>(sum, over ? 1 : 0, ex, ex2, &tot, &tot2, wsum);
+        if (tot2 == 0 && tot <= kCandCap) {
+            int off = ex;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * (int)threadIdx.x + i;
+                if (c < ncc) coff[c] = off;
+                off += mine[i];
+            }
+            if (threadIdx.x == 0) coff[ncc] = tot;
+            __syncthreads();
+            const float* src = ccand + oh * (size_t)ncc * kCandPerChunk;
+            for (int e = threadIdx.x; e < tot; e += 256) {
+                int lo_c = 0, hi_c = ncc - 1;            // last chunk with coff[c] <= e
+                while (lo_c < hi_c) {
+                    const int mid = (lo_c + hi_c + 1) >> 1;
+                    if (coff[mid] <= e) lo_c = mid; else hi_c = mid - 1;
+                }
+                cand[e] = src[(size_t)lo_c * kCandPerChunk + (e - coff[lo_c])];
+            }
+            __syncthreads();
+            ncand = tot;
+            gathered = true;
+        }
+    }
+    for (int base = 0; !gathered && base < nused; base += 256) {
         const int sl = base + threadIdx.x;
         const float x = sl < nused ? a * lrow[sl] : -INFINITY;
         const bool f = x > lo;
@@ -351,6 +396,76 @@ static __global__ __launch_bounds__(256) void tau_kernel(
         if (delta_out) delta_out[oh] = 1.0f - ref.s1;
         if (supref_out) supref_out[oh] = (int32_t)ref.k;
     }
+}
+
+
+// Threshold candidates of the general entmax path, compacted by many blocks:
+// grid (ncc, HQ, B), block c of head (b, h) takes slots
+// [c*kCandChunk, (c+1)*kCandChunk) and writes its x = (alpha-1) s > max(x) - 1
+// in slot order to its own list of kCandPerChunk entries, with the count
+// (-1 when the list would overflow).  max(x) comes from the logits kernel's
+// chunk partials, combined as tau_kernel combines them, so tau_kernel can
+// gather the lists in chunk order into exactly the array it would build.
+static __global__ __launch_bounds__(256) void cand_kernel(
+    const float* __restrict__ logits, const float* __restrict__ part1,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
+    float alpha, int ncc, float* __restrict__ ccand, int32_t* __restrict__ ccnt) {
+    __shared__ float red[8];
+    __shared__ int wsum[8];
+    int phase = 0;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int R = HQ / G;
+    const int unit = b * G + h / R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int nused = cnt * kPage;
+    const size_t oh = (size_t)b * HQ + h;
+    int32_t* count = ccnt + oh * ncc + c;
+    const int s0 = c * kCandChunk;
+    if (s0 >= nused) {                       // block-uniform
+        if (threadIdx.x == 0) *count = 0;
+        return;
+    }
+    const float* pm = part1 + oh * nchunk1 * 3;
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < nchunk1; i += 256) mx = fmaxf(mx, pm[i * 3]);
+    mx = block_max<4>(mx, red, phase);
+    const float a = alpha - 1.0f;
+    const float lo = a * mx - 1.0f;
+    // 16 consecutive slots per thread; nused is a multiple of 16 (whole
+    // pages), so a thread's slots are all used or all unused.
+    const int sb = s0 + 16 * (int)threadIdx.x;
+    float x[16];
+    if (sb < nused) {
+        const float4* p4 = reinterpret_cast<const float4*>(logits + oh * nslot + sb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = p4[i];
+            x[4 * i] = a * v.x;
+            x[4 * i + 1] = a * v.y;
+            x[4 * i + 2] = a * v.z;
+            x[4 * i + 3] = a * v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = -INFINITY;
+    }
+    int k = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) k += x[i] > lo ? 1 : 0;
+    int ex, ex2, tot, tot2;
+    block_excl_scan2<4>(k, 0, ex, ex2, &tot, &tot2, wsum);
+    if (!(mx > -INFINITY) || tot > kCandPerChunk) {
+        if (threadIdx.x == 0) *count = mx > -INFINITY ? -1 : 0;
+        return;
+    }
+    float* dst = ccand + (oh * ncc + c) * kCandPerChunk;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (x[i] > lo) dst[ex++] = x[i];
+    if (threadIdx.x == 0) *count = tot;
 }
 
 // ------------------------------------------------------------------ PV ----
@@ -924,9 +1039,20 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    float* ccand = pl.ncc ? (float*)(ws + pl.off_cand) : nullptr;
+    int32_t* ccnt = pl.ncc ? (int32_t*)(ws + pl.off_ccnt) : nullptr;
+    if (ccand && mode != kModeSoftmax) {
+        cand_kernel<<<dim3(pl.ncc, d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count,
+                                                                  sel_stride, d.G, d.HQ, d.MP, pl.nslot,
+                                                                  pl.nchunk1, alpha, pl.ncc, ccand, ccnt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        ccand = nullptr;
+    }
     tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
                                                      d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
-                                                     tau_ref, tau, support, delta, supref);
+                                                     tau_ref, tau, support, delta, supref, ccand, ccnt, pl.ncc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(

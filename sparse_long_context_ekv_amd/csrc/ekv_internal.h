@@ -55,7 +55,8 @@ struct DecodePlan {
     int nchunk1;     // logits blocks per (b, g)
     int spb;         // slots per PV block (multiple of 256)
     int nchunk3;     // PV blocks per (b, g)
-    size_t off_logits, off_part1, off_part3, bytes;
+    int ncc;         // threshold-candidate chunks per (b, h) (general entmax path), 0 = none
+    size_t off_logits, off_part1, off_part3, off_cand, off_ccnt, bytes;
 };
 DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha);
 hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,

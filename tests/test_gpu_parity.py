@@ -38,6 +38,14 @@ def workload(name):
         g = torch.Generator(device="cuda").manual_seed(11)
         wl.k_cache.copy_((torch.randn(wl.k_cache.shape, generator=g, device="cuda") * 0.02).to(wl.k_cache.dtype))
         return wl
+    if name == "flat-long":
+        # flat keys over several 4096-slot candidate chunks: in the full-cache
+        # path every chunk has more threshold candidates than it may hand over,
+        # so the threshold kernel compacts them itself
+        wl = W.make_workload(W.CONFIGS[2].scaled(batch=2), "cuda", seq_lens=[12000, 5000])
+        g = torch.Generator(device="cuda").manual_seed(12)
+        wl.k_cache.copy_((torch.randn(wl.k_cache.shape, generator=g, device="cuda") * 0.02).to(wl.k_cache.dtype))
+        return wl
     raise KeyError(name)
 
 
@@ -320,8 +328,13 @@ def _support_slack(s_row, tau, alpha):
 
 @pytest.mark.parametrize("name,alpha", [("tiny", 1.5), ("tiny", 2.0), ("tiny", 1.0), ("tiny", 4.0 / 3.0),
                                         ("tiny", 3.0), ("llama-ragged", 1.5), ("llama-ragged", 1.0),
-                                        ("llama-ragged", 2.0)])
+                                        ("llama-ragged", 2.0), ("llama-ragged", 4.0 / 3.0), ("llama-ragged", 3.0),
+                                        ("flat-long", 1.5)])
 def test_full_cache_decode(name, alpha):
+    """Full-cache decode (every token) against the oracle.  Rows of more
+    than 4096 slots take the multi-block threshold-candidate compaction
+    (llama-ragged: 5000 tokens), or its fallback when a chunk holds too many
+    candidates (flat-long)."""
     wl = workload(name)
     c = wl.cfg
     out, tau, sup, _, _ = _run_decode(wl, alpha)
