@@ -586,14 +586,37 @@ __global__ __launch_bounds__(256) void pv_kernel(
     }
 }
 
-static __global__ void reduce_kernel(const float* __restrict__ part3, int HQ, int D, int nchunk3,
-                              float* __restrict__ out) {
+// kReduceThreads threads per (b, h): thread (slice, c) sums the chunks
+// k = slice, slice + S, ... (S = kReduceThreads / D slices) of channel c in
+// order, then slice 0 adds the S slice sums in slice order: a fixed order,
+// with S independent load streams per channel instead of one (one stream took
+// 80 us over the 256 chunks of a 1M-token row).
+constexpr int kReduceThreads = 1024;
+static __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const float* __restrict__ part3, int HQ, int D,
+                                                                      int nchunk3, float* __restrict__ out) {
+    __shared__ float red[kReduceThreads];
     const int h = blockIdx.x, b = blockIdx.y;
     const size_t oh = (size_t)b * HQ + h;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-        float s = 0.0f;
-        for (int k = 0; k < nchunk3; ++k) s += part3[(oh * nchunk3 + k) * D + c];
-        out[oh * D + c] = s;
+    const int S = kReduceThreads / D;
+    const int slice = threadIdx.x / D, c = threadIdx.x - slice * D;
+    const float* src = part3 + oh * nchunk3 * D + c;
+    float s = 0.0f;
+    int k = slice;
+    for (; k + 3 * S < nchunk3; k += 4 * S) {
+        const float a0 = src[(size_t)k * D], a1 = src[(size_t)(k + S) * D];
+        const float a2 = src[(size_t)(k + 2 * S) * D], a3 = src[(size_t)(k + 3 * S) * D];
+        s += a0;
+        s += a1;
+        s += a2;
+        s += a3;
+    }
+    for (; k < nchunk3; k += S) s += src[(size_t)k * D];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    if (slice == 0) {
+        float t = red[c];
+        for (int i = 1; i < S; ++i) t += red[i * D + c];
+        out[oh * D + c] = t;
     }
 }
 
@@ -1060,7 +1083,7 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         pl.nslot, pl.spb, pl.nchunk3, mode, alpha, beta, part3);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    reduce_kernel<<<dim3(d.HQ, d.B), dim3(D), 0, s>>>(part3, d.HQ, D, pl.nchunk3, out);
+    reduce_kernel<<<dim3(d.HQ, d.B), dim3(kReduceThreads), 0, s>>>(part3, d.HQ, D, pl.nchunk3, out);
     return hipGetLastError();
 }
 
