@@ -479,6 +479,7 @@ __global__ __launch_bounds__(256) void pv_kernel(
     constexpr int CH = D / kRow;
     __shared__ int list_slot[256];
     __shared__ float list_p[256][R];
+    __shared__ int pg_phys[256 / kPage];    // physical tile of each page of the current 256-slot batch
     __shared__ int wsum[4];
     __shared__ float wred[4][R][D];
     const int unit = blockIdx.y;
@@ -506,6 +507,21 @@ __global__ __launch_bounds__(256) void pv_kernel(
         for (int c = 0; c < CH; ++c) acc[j][c] = 0.0f;
 
     for (int base = s0; base < s1; base += 256) {
+        // The batch's 16 pages resolved once (selection -> page table), so
+        // that the V row loads below depend on nothing but LDS.  base is a
+        // multiple of 256 (s0 is a multiple of spb).
+        if (threadIdx.x < 256 / kPage) {
+            const int ip = (base >> 4) + (int)threadIdx.x;
+            int phys = -1;
+            if (ip * kPage < s1) {
+                const int lp = sel ? sel[ip] : ip;
+                if (lp >= 0 && lp < M) {
+                    const int ph = page_table[(size_t)b * MP + lp];
+                    phys = (ph >= 0 && ph < NP) ? ph : -1;
+                }
+            }
+            pg_phys[threadIdx.x] = phys;
+        }
         const int sl = base + threadIdx.x;
         float pj[R];
         bool any = false;
@@ -541,20 +557,33 @@ __global__ __launch_bounds__(256) void pv_kernel(
             for (int j = 0; j < R; ++j) list_p[pos][j] = pj[j];
         }
         __syncthreads();
-        for (int e = row; e < tot; e += kRow) {
-            const int slot = list_slot[e];
-            const int ip = slot >> 4, t = slot & (kPage - 1);
-            const int lp = sel ? sel[ip] : ip;
-            if (lp < 0 || lp >= M) continue;
-            const int phys = page_table[(size_t)b * MP + lp];
-            if (phys < 0 || phys >= NP) continue;
-            Vec<T, CH> vv;
-            vv.load(v_cache + (((size_t)phys * G + g) * kPage + t) * D + lane * CH);
+        // Each row takes entries row, row + 16, ... in order, four V rows in
+        // flight at a time, without branches between the loads (an empty or
+        // invalid entry reads row 0 of tile 0 and is ignored).
+        constexpr int PVB = 4;
+        for (int e0 = row; e0 < tot; e0 += PVB * kRow) {
+            Vec<T, CH> vv[PVB];
+            bool ok[PVB];
+            int ent[PVB];
 #pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const float p = list_p[e][j];
+            for (int u = 0; u < PVB; ++u) {
+                const int e = e0 + u * kRow;
+                ent[u] = e < tot ? e : e0;
+                const int slot = list_slot[ent[u]];
+                const int phys = pg_phys[(slot - base) >> 4];
+                ok[u] = e < tot && phys >= 0;
+                vv[u].load(v_cache + (((size_t)(ok[u] ? phys : 0) * G + g) * kPage + (slot & (kPage - 1))) * D +
+                           lane * CH);
+            }
 #pragma unroll
-                for (int c = 0; c < CH; ++c) acc[j][c] = fmaf(p, vv.get(c), acc[j][c]);
+            for (int u = 0; u < PVB; ++u) {
+                if (!ok[u]) continue;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const float p = list_p[ent[u]][j];
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) acc[j][c] = fmaf(p, vv[u].get(c), acc[j][c]);
+                }
             }
         }
         __syncthreads();
