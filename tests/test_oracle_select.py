@@ -164,3 +164,28 @@ def test_gauss_margin_zero_sigma():
     sig = np.zeros((1, 3))
     t = sel.gauss_margins(mu, sig, np.array([0.5]), 1.5)     # theta = 1.0
     assert t[0] == -np.inf and t[1] == -np.inf and t[2] == np.inf
+
+
+def test_chunked_selection_equals_one_level():
+    """The decomposition behind the GPU's two-level selection of long rows:
+    under the order "larger key first, then lower page index", keeping the
+    top min(k, chunk) pages of every chunk and then the top k of their union
+    (kept in page order) gives exactly the one-level top k, with exact ties,
+    chunks of any size and a partial last chunk.  Also with a cutoff: the
+    count of keys at or above it, summed over chunks, decides how many pages
+    the one-level rule keeps (max(1, min(k, count)))."""
+    rng = np.random.default_rng(31)
+    for _ in range(300):
+        M = int(rng.integers(1, 400))
+        k = int(rng.integers(1, 60))
+        C = int(rng.integers(1, 70))
+        U = rng.integers(-6, 7, size=M).astype(float)          # many exact ties
+        cut = float(rng.integers(-6, 8))
+        union = np.concatenate([c0 + sel.topk_pages(U[c0:c0 + C], k) for c0 in range(0, M, C)])
+        assert np.all(np.diff(union) > 0)                     # page order
+        count = sum(int(np.count_nonzero(U[c0:c0 + C] >= cut)) for c0 in range(0, M, C))
+        keep = max(1, min(k, count))
+        got = union[sel.topk_pages(U[union], keep)]
+        want = sel.topk_pages(U, keep)
+        np.testing.assert_array_equal(got, want)
+        assert count == int(np.count_nonzero(U >= cut))
