@@ -194,6 +194,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="also time steps that each follow a 512 MiB read, which evicts the 256 MB Infinity "
+                         "Cache (for workloads whose per-step bytes fit in it); reported as mall_flushed")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many bytes "
                          "(a kernel of known traffic for scaling hardware byte counters)")
@@ -287,6 +290,32 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": sk_bytes, "avg_launch_us": round(sk_us, 2)},
     }
+
+    if args.flush_mall:
+        # Each step follows a read of a 512 MiB buffer (outside its events), so
+        # nothing it reads can come from the Infinity Cache left by the
+        # previous step.  A read, not a write: evicting dirty lines would be
+        # written back during the step and slow it instead.
+        junk = torch.ones(128 * 2**20, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b2, c2 in fe:
+            junk.sum()
+            a.record(stream)
+            dec.score()
+            b2.record(stream)
+            dec.select()
+            dec.decode()
+            c2.record(stream)
+        torch.cuda.synchronize()
+        del junk
+        f_step = statistics.median([a.elapsed_time(c2) for a, _, c2 in fe])
+        f_score = statistics.mean([a.elapsed_time(b2) for a, b2, _ in fe]) * 1e3
+        result["mall_flushed"] = {"median_event_ms_per_step": round(f_step, 4), "score_kernel_us": round(f_score, 2),
+                                  "score_kernel_gbps": round(sk_bytes / (f_score * 1e-6) / 1e9, 1),
+                                  "note": "each step after a 512 MiB read; HIP events around each step"}
+        log(f"after a cache-evicting read: median step {f_step:.4f} ms (events), score kernel {f_score:.1f} us")
 
     # Quality of the selection: dropped mass against the full-cache threshold.
     def time_full(runner, reps=5):
