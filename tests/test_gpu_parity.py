@@ -38,6 +38,9 @@ def workload(name):
         g = torch.Generator(device="cuda").manual_seed(11)
         wl.k_cache.copy_((torch.randn(wl.k_cache.shape, generator=g, device="cuda") * 0.02).to(wl.k_cache.dtype))
         return wl
+    if name == "long-with-empty":
+        # an empty sequence beside rows of several candidate chunks
+        return W.make_workload(W.CONFIGS[2].scaled(batch=3), "cuda", seq_lens=[9000, 0, 37])
     if name == "flat-long":
         # flat keys over several 4096-slot candidate chunks: in the full-cache
         # path every chunk has more threshold candidates than it may hand over,
@@ -329,17 +332,22 @@ def _support_slack(s_row, tau, alpha):
 @pytest.mark.parametrize("name,alpha", [("tiny", 1.5), ("tiny", 2.0), ("tiny", 1.0), ("tiny", 4.0 / 3.0),
                                         ("tiny", 3.0), ("llama-ragged", 1.5), ("llama-ragged", 1.0),
                                         ("llama-ragged", 2.0), ("llama-ragged", 4.0 / 3.0), ("llama-ragged", 3.0),
-                                        ("flat-long", 1.5)])
+                                        ("flat-long", 1.5), ("long-with-empty", 1.5), ("long-with-empty", 1.0)])
 def test_full_cache_decode(name, alpha):
     """Full-cache decode (every token) against the oracle.  Rows of more
     than 4096 slots take the multi-block threshold-candidate compaction
     (llama-ragged: 5000 tokens), or its fallback when a chunk holds too many
-    candidates (flat-long)."""
+    candidates (flat-long); an empty sequence gives out 0, tau -inf and
+    support 0 (entmax over no token is undefined)."""
     wl = workload(name)
     c = wl.cfg
     out, tau, sup, _, _ = _run_decode(wl, alpha)
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
+        if n == 0:
+            assert bool((out[b] == 0).all()) and bool((tau[b] == -float("inf")).all())
+            assert bool((sup[b] == 0).all())
+            continue
         ref = oracle.decode.decode(q, K, V, None, alpha)
         assert np.abs(H.to_np(out[b]) - ref["out"]).max() <= H.OUT_ATOL
         for h in range(c.num_q_heads):

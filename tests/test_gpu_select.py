@@ -184,3 +184,22 @@ def test_superset_select_two_level(MP, theta, lo, hi):
             assert c == len(want), (b, g, c, len(want))
             np.testing.assert_array_equal(sel[b, g, :c], want)
             assert np.all(sel[b, g, c:] == -1)
+
+
+def test_two_level_select_empty_and_short_rows():
+    """Few long rows (two-level path) beside an empty row and rows shorter
+    than one chunk or than the budget."""
+    print("[case] two-level empty/short", flush=True)
+    B, G, budget, MP = 4, 2, 128, 20000
+    lens = [0, MP * P, 100 * P - 3, 4100 * P]
+    rng = np.random.default_rng(404)
+    score = rng.standard_normal((B, G, MP)).astype(np.float32)
+    sel, cnt, _ = _run_select(_shape(B, G, 1, MP), ekv.SEL_TOPK, lens, 1.5, budget, 3.0,
+                              score=torch.from_numpy(score).cuda())
+    assert np.all(cnt[0] == 0) and np.all(sel[0] == -1)
+    for b in range(1, B):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            U = score[b, g, :M].astype(np.float64)
+            want = oracle.select.topk_pages(U, budget)
+            _check_rows(sel, cnt, b, g, want, U, budget)
