@@ -359,13 +359,17 @@ def test_full_cache_decode(name, alpha):
 @pytest.mark.parametrize("name,alpha", [("tiny", 1.5), ("tiny", 2.0), ("tiny", 1.0), ("tiny", 4.0 / 3.0),
                                         ("tiny", 3.0), ("llama-ragged", 1.5), ("llama-ragged", 1.0),
                                         ("llama-ragged", 2.0), ("gauss-ragged", 1.5), ("flat", 1.5), ("flat", 2.0),
-                                        ("flat", 4.0 / 3.0)])
+                                        ("flat", 4.0 / 3.0), ("llama-ragged-wide", 1.5), ("llama-ragged-wide", 1.0),
+                                        ("llama-ragged-wide", 2.0)])
 def test_sparse_decode_on_oracle_selection(name, alpha):
     """Decode over a given selection (the oracle's top-k), with the dropped
-    mass measured against the full-cache threshold."""
-    wl = workload(name)
+    mass measured against the full-cache threshold.  "llama-ragged-wide"
+    selects 300 pages (4800 slots) per group: past the fused kernel's 4096
+    slots, so it takes the general path (and, for entmax, the multi-block
+    threshold-candidate compaction) with a selection."""
+    wl = workload("llama-ragged" if name == "llama-ragged-wide" else name)
     c = wl.cfg
-    budget = {"gauss-ragged": 64, "flat": 256}.get(name, c.budget_pages)
+    budget = {"gauss-ragged": 64, "flat": 256, "llama-ragged-wide": 300}.get(name, c.budget_pages)
     sels, fulls = [], []
     for b in range(c.batch):
         q, K, V, n = H.seq_logical(wl, b)
