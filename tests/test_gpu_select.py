@@ -203,3 +203,37 @@ def test_two_level_select_empty_and_short_rows():
             U = score[b, g, :M].astype(np.float64)
             want = oracle.select.topk_pages(U, budget)
             _check_rows(sel, cnt, b, g, want, U, budget)
+
+
+def test_gauss_select_one_level_global_kernel():
+    """256 (sequence, group) rows of 70000 pages in Gaussian mode: the
+    one-level global-memory selection kernel and the threshold kernel
+    without LDS staging (rows past its LDS capacity); sampled rows against
+    the oracle."""
+    print("[case] gauss one-level global", flush=True)
+    B, G, R, MP, budget, z, alpha = 64, 4, 4, 70000, 256, 3.0, 1.5
+    lens = [MP * P - 11 * (b % 5) for b in range(B)]
+    rng = np.random.default_rng(70001)
+    mu = (rng.standard_normal((B, G * R, MP)) * 0.25).astype(np.float32)
+    sg = (0.8 + 0.4 * rng.random((B, G * R, MP))).astype(np.float32)
+    sel, cnt, th = _run_select(_shape(B, G, R, MP), ekv.SEL_GAUSS, lens, alpha, budget, z,
+                               mu=torch.from_numpy(mu).cuda(), sigma=torch.from_numpy(sg).cuda())
+    for b in (0, B - 1):
+        n = lens[b]
+        M = (n + P - 1) // P
+        n_p = oracle.paged.page_valid_counts(n, P)
+        for h in range(G * R):
+            want = oracle.select.gauss_tau_hat(mu[b, h, :M].astype(np.float64), sg[b, h, :M].astype(np.float64),
+                                               n_p, alpha)
+            assert H.tau_close(th[b, h], want), (b, h, th[b, h], want)
+        for g in range(G):
+            hs = slice(g * R, (g + 1) * R)
+            m64, s64 = mu[b, hs, :M].astype(np.float64), sg[b, hs, :M].astype(np.float64)
+            t = oracle.select.gauss_margins(m64, s64, th[b, hs], alpha)
+            want = oracle.select.gauss_select(m64, s64, th[b, hs], alpha, z, budget)
+            c = int(cnt[b, g])
+            row = sel[b, g]
+            assert c == len(want) or np.any(np.abs(t + z) < 1e-4 * z)
+            assert np.all(row[c:] == -1) and np.all(np.diff(row[:c]) > 0)
+            if c == len(want):
+                H.compare_selection(row[:c], want, t, len(want))
