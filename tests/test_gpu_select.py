@@ -237,3 +237,34 @@ def test_gauss_select_one_level_global_kernel():
             assert np.all(row[c:] == -1) and np.all(np.diff(row[:c]) > 0)
             if c == len(want):
                 H.compare_selection(row[:c], want, t, len(want))
+
+
+def test_superset_select_one_level_global_kernel():
+    """The superset rule on 256 rows of 70000 pages (one-level global-memory
+    kernel); integer box scores and a threshold halfway between integers, as
+    in the two-level case; sampled rows against the oracle."""
+    print("[case] superset one-level global", flush=True)
+    B, G, budget, alpha, MP, theta = 128, 2, 200, 1.5, 70000, 995.5
+    lens = [MP * P - 7 * (b % 3) for b in range(B)]
+    rng = np.random.default_rng(70002)
+    score = rng.integers(-1000, 1001, size=(B, G, MP)).astype(np.float32)
+    sh = _shape(B, G, 1, MP)
+    sel = torch.full((B, G, budget), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    tau_lo = torch.full((B, G), theta * (alpha - 1.0), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ekv.select_workspace_bytes(sh, ekv.SEL_SUPERSET, alpha, budget, 3.0), dtype=torch.uint8,
+                     device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ekv.select(sh, ekv.SEL_SUPERSET, sl, alpha, budget, 3.0, torch.from_numpy(score).cuda(), None, None, sel, cnt,
+               tau_lo, ws)
+    H.sync()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(0, B, 17):
+        M = (lens[b] + P - 1) // P
+        for g in range(G):
+            want = oracle.select.superset_pages(score[b, g, :M].astype(np.float64),
+                                                np.array([theta * (alpha - 1.0)]), alpha, budget)
+            c = int(cnt[b, g])
+            assert c == len(want), (b, g, c, len(want))
+            np.testing.assert_array_equal(sel[b, g, :c], want)
+            assert np.all(sel[b, g, c:] == -1)
