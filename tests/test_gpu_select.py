@@ -268,3 +268,30 @@ def test_superset_select_one_level_global_kernel():
             assert c == len(want), (b, g, c, len(want))
             np.testing.assert_array_equal(sel[b, g, :c], want)
             assert np.all(sel[b, g, c:] == -1)
+
+
+@pytest.mark.parametrize("G,R", [(4, 2), (1, 8)])
+def test_gauss_select_two_level_group_sizes(G, R):
+    """Two-level Gaussian selection with 2 and 8 query heads per KV group."""
+    print(f"[case] gauss two-level G={G} R={R}", flush=True)
+    B, MP, budget, z, alpha = 2, 20000, 256, 3.0, 1.5
+    lens = [MP * P - 5, 12345 * P]
+    rng = np.random.default_rng(100 * G + R)
+    mu = (rng.standard_normal((B, G * R, MP)) * 0.25).astype(np.float32)
+    sg = (0.8 + 0.4 * rng.random((B, G * R, MP))).astype(np.float32)
+    sel, cnt, th = _run_select(_shape(B, G, R, MP), ekv.SEL_GAUSS, lens, alpha, budget, z,
+                               mu=torch.from_numpy(mu).cuda(), sigma=torch.from_numpy(sg).cuda())
+    for b in range(B):
+        n = lens[b]
+        M = (n + P - 1) // P
+        for g in range(G):
+            hs = slice(g * R, (g + 1) * R)
+            m64, s64 = mu[b, hs, :M].astype(np.float64), sg[b, hs, :M].astype(np.float64)
+            t = oracle.select.gauss_margins(m64, s64, th[b, hs], alpha)
+            want = oracle.select.gauss_select(m64, s64, th[b, hs], alpha, z, budget)
+            c = int(cnt[b, g])
+            row = sel[b, g]
+            assert c == len(want) or np.any(np.abs(t + z) < 1e-4 * z)
+            assert np.all(row[c:] == -1) and np.all(np.diff(row[:c]) > 0)
+            if c == len(want):
+                H.compare_selection(row[:c], want, t, len(want))
