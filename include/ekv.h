@@ -58,6 +58,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* ABI version of this header (ekv_abi_version() returns it). */
+#define EKV_ABI_VERSION 3
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -106,7 +109,9 @@ typedef struct {
  *               (fp32 accumulation in token order; rounded to stat_dtype).
  * Results are written at the page's PHYSICAL index.
  *   page_list : NULL = every logical page of every sequence; otherwise n_list
- *               device entries b*MP + p (entries with p >= M_b are skipped).
+ *               device entries b*MP + p (negative entries, entries with
+ *               b >= B or p >= M_b, and pages whose page_table entry lies
+ *               outside [0, NP) are skipped).
  *   kmin,kmax : may both be NULL (not written); kmean,kvar likewise; not all
  *               four NULL.
  * Not on the per-step path: run at prefill or when a page fills.          */
@@ -145,7 +150,9 @@ ekv_status ekv_append_kv(const ekv_shape* shape, const void* k_new, const void* 
  *   sigma_{h,p} = sqrt((1/D) sum_i q_{h,i}^2 kvar_{p,i})
  *   (per-head moments of the page's token scores, channels treated as
  *   independent).
- * Entries for p >= M_b are not written.  Accumulation is fp32.            */
+ * Entries for p >= M_b are not written.  A page p < M_b whose page_table
+ * entry lies outside [0, NP) is not read: it gets score -inf, or mu -inf and
+ * sigma 0 (a point mass below every threshold).  Accumulation is fp32.     */
 ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void* q,
                            const int32_t* page_table, const int32_t* seq_lens,
                            const void* kmin, const void* kmax,
@@ -225,7 +232,8 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
 /* Message describing the last error returned on this thread ("" if none). */
 const char* ekv_last_error(void);
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version; equals EKV_ABI_VERSION of the header it was built
+ * with. */
 int32_t ekv_abi_version(void);
 
 #ifdef __cplusplus

@@ -77,7 +77,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 extern "C" {
 
-int32_t ekv_abi_version(void) { return 3; }
+int32_t ekv_abi_version(void) { return EKV_ABI_VERSION; }
 
 const char* ekv_last_error(void) { return g_err; }
 

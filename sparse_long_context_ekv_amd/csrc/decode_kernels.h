@@ -830,8 +830,13 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
                     if (xr[k][c] > lo) fn(xr[k][c], base + k * 256 + 4 * lane + c);
         }
     };
-    // Sum of the head's W wave partials (fixed order), after a barrier.
-    int pb = 1;
+    // Sum of the head's W wave partials (fixed order), after a barrier.  The
+    // partials alternate between part[0] and part[1]: a call writes the
+    // buffer that the call before the previous one read, and the previous
+    // call's barrier lies between those reads and this write.  Step 1 above
+    // read part[0] with no barrier after it, so the first call must write
+    // part[1] (pb starts at 0 and is flipped before the write).
+    int pb = 0;
     auto head_sums = [&](float v0, float v1, float v2, float v3, int fl, float* r, bool& any) {
         pb ^= 1;
         if (lane == 0) {

@@ -21,6 +21,8 @@
 // the [B][.][MP] rows (one per page and head) cost the statistics stream a
 // third of its speed, and stores interleaved with the stream cost twice what
 // they cost alone.
+#include <atomic>
+
 #include "ekv_device.h"
 #include "ekv_internal.h"
 
@@ -118,7 +120,14 @@ __global__ __launch_bounds__(256) void box_score_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (!ok[u]) continue;
+            if (!ok[u]) {
+                // a page of the block whose table entry maps outside the
+                // cache: defined result -inf (never selected ahead of a
+                // readable page), not a stale stage slot
+                if (p0 + u * per_iter < p_end && lane == 0)
+                    stage[(g << lg_ppb) + p0 + u * per_iter - p_begin] = -INFINITY;
+                continue;
+            }
             float best = -INFINITY;
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -203,7 +212,14 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (!ok[u]) continue;
+            if (!ok[u]) {
+                // table entry outside the cache: mu = -inf, sigma = 0, a point
+                // mass that adds nothing to the threshold equation and has
+                // the lowest margin (never a stale stage slot)
+                if (p0 + u * per_iter < p_end && writer)
+                    dst[p0 + u * per_iter - p_begin] = lane < R ? -INFINITY : 0.0f;
+                continue;
+            }
             float mine = 0.0f;
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -243,18 +259,21 @@ static int score_lg_ppb(const Dims& d, int out_per_page, int lg_max) {
     return lg;
 }
 
+// Raises the kernel's dynamic LDS limit to 64 KiB, once per device.  The flag
+// is atomic so that concurrent first calls from several host threads are
+// well defined (setting the attribute twice is harmless).
 template <typename K>
 static bool allow_64k_lds(K kernel) {
-    static bool ok[64] = {};
+    static std::atomic<bool> ok[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!ok[dev]) {
+    if (!ok[dev].load(std::memory_order_acquire)) {
         if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 65536) == hipSuccess)
-            ok[dev] = true;
+            ok[dev].store(true, std::memory_order_release);
         else
             (void)hipGetLastError();
     }
-    return ok[dev];
+    return ok[dev].load(std::memory_order_acquire);
 }
 
 template <typename T, int D, int R>

@@ -24,6 +24,8 @@
 // ties going to the lower page index.  The k-th largest key is found by an
 // 8-bit radix select over order-preserving 32-bit keys; the kept pages are
 // then compacted in index order, which yields ascending output.
+#include <atomic>
+
 #include "ekv_device.h"
 #include "ekv_internal.h"
 
@@ -823,20 +825,23 @@ static hipError_t run_gauss_tau(const Dims& d, const float* mu, const float* sig
     // (a*mu, a*sigma) are staged in LDS for sequences of up to kTauLdsPages
     // pages (64 KiB of the 160 KiB a gfx950 workgroup may use).  The kernel
     // attribute allowing that much dynamic LDS is set once per device.
-    static bool attr_ok[64] = {};
+    // The flag is atomic: concurrent first calls from several host threads
+    // are well defined (setting the attribute twice is harmless).
+    static std::atomic<bool> attr_ok[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     const size_t max_lds = (size_t)(kTauLdsPages + kTauLdsPages / kTauSub) * sizeof(float2);
-    if (!attr_ok[dev]) {
+    if (!attr_ok[dev].load(std::memory_order_acquire)) {
         if (hipFuncSetAttribute((const void*)gauss_tau_kernel<BETA>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)max_lds) == hipSuccess)
-            attr_ok[dev] = true;
+            attr_ok[dev].store(true, std::memory_order_release);
         else
             (void)hipGetLastError();
     }
+    const bool big = attr_ok[dev].load(std::memory_order_acquire);
     // lds_pages is a multiple of kTauSub: the subsample array follows the pages.
-    int lds_pages = attr_ok[dev] ? (d.MP < kTauLdsPages ? d.MP : kTauLdsPages) : 0;
-    if (!attr_ok[dev] && (size_t)d.MP * sizeof(float2) * (kTauSub + 1) / kTauSub <= 48 * 1024) lds_pages = d.MP;
+    int lds_pages = big ? (d.MP < kTauLdsPages ? d.MP : kTauLdsPages) : 0;
+    if (!big && (size_t)d.MP * sizeof(float2) * (kTauSub + 1) / kTauSub <= 48 * 1024) lds_pages = d.MP;
     lds_pages = (lds_pages + kTauSub - 1) / kTauSub * kTauSub;
     const size_t lds = (size_t)(lds_pages + lds_pages / kTauSub) * sizeof(float2);
     gauss_tau_kernel<BETA><<<dim3(d.HQ, d.B), dim3(kTauThreads), lds, s>>>(

@@ -124,8 +124,9 @@ __global__ __launch_bounds__(256) void page_stats_kernel(
     const int g = row % G;
     for (int item = blockIdx.x * per_iter + row / G; item < n_items; item += gridDim.x * per_iter) {
         int e = page_list ? page_list[item] : item;
+        if (e < 0) continue;                      // a negative entry would divide to b = 0, p < 0
         int b = e / MP, p = e - b * MP;
-        if (b < 0 || b >= B) continue;
+        if (b >= B) continue;
         int n = seq_len_at(seq_lens, b, MP);
         if (p >= num_pages(n)) continue;
         int np = min(kPage, n - p * kPage);

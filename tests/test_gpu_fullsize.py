@@ -56,6 +56,56 @@ def _gpu_selection(dec, b, G):
     return [dec.buf.sel_pages[b, g, :int(dec.buf.sel_count[b, g])].cpu().numpy() for g in range(G)]
 
 
+def test_llama3_8b_layer_32k_fullsize():
+    """The Llama-3-8B-shaped layer at its stated size: B=1, 32/8 heads,
+    d=128, 32768 tokens, 64 planted keys per group, top-k 128 pages, in the
+    bench's launch configuration.  The whole sequence goes to the oracle:
+    statistics of all 2048 pages, every box score, the exact top-128, decode
+    on the selection, the full-cache decode over every token, and the
+    dropped mass against it."""
+    cfg = W.CONFIGS[2]
+    print(f"[case] {cfg.name}", flush=True)
+    wl = W.make_workload(cfg, "cuda")
+    alpha = 1.5
+    dec = ekv.Decoder(wl, "topk", alpha, cfg.budget_pages)
+    dec.build_stats()
+    dec.step()
+    full = ekv.FullDecoder(wl, alpha)
+    full.run()
+    delta = torch.empty_like(dec.buf.tau)
+    supref = torch.empty_like(dec.buf.support)
+    dec.decode(tau_ref=full.tau, delta=delta, support_ref=supref)
+    H.sync()
+    G, HQ = cfg.num_kv_groups, cfg.num_q_heads
+    r = HQ // G
+    b = 0
+    q, K, V, n = H.seq_logical(wl, b)
+    kmin, kmax, mean, var = oracle.paged.page_stats(K, P)
+    rows = H.phys_rows(wl, b)
+    np.testing.assert_array_equal(H.to_np(dec.stats["kmin"][rows]), kmin)
+    np.testing.assert_array_equal(H.to_np(dec.stats["kmax"][rows]), kmax)
+    _, U = oracle.paged.box_scores(q, kmin, kmax)
+    M = U.shape[1]
+    np.testing.assert_allclose(H.to_np(dec.buf.score[b, :, :M]), U, rtol=1e-5, atol=1e-5 * np.abs(U).max())
+    sels = _gpu_selection(dec, b, G)
+    for g in range(G):
+        want = oracle.select.topk_pages(U[g], cfg.budget_pages)
+        H.compare_selection(sels[g], want, U[g], len(want))
+    _check_decode_on_selection(wl, dec, b, q, alpha, sels)
+    ref = oracle.decode.decode(q, K, V, None, alpha)
+    assert np.abs(H.to_np(full.out[b]) - ref["out"]).max() <= H.OUT_ATOL
+    for h in range(HQ):
+        assert H.tau_close(float(full.tau[b, h]), ref["tau"][h]), (h, float(full.tau[b, h]), ref["tau"][h])
+        toks = oracle.decode.tokens_of_pages(sels[h // r], n, P)
+        d_or = 1.0 - ref["p"][h][toks].sum()
+        assert abs(float(delta[b, h]) - d_or) <= H.DELTA_ATOL, (h, float(delta[b, h]), d_or)
+        kept = int(np.count_nonzero(ref["p"][h][toks] > 0))
+        x = (alpha - 1.0) * ref["s"][h][toks]
+        slack = int(np.count_nonzero(np.abs(x - ref["tau"][h]) < 1e-5 * max(1.0, abs(ref["tau"][h]))))
+        assert abs(int(supref[b, h]) - kept) <= slack
+    del dec, full, wl
+
+
 def test_batched_128k_gaussian_fullsize():
     """The headline workload: B=16, 32/8 heads, d=128, 131072 tokens each,
     Gaussian selector capped at 256 pages, fp32 statistics."""
