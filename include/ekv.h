@@ -59,7 +59,7 @@
 #include <stdint.h>
 
 /* ABI version of this header (ekv_abi_version() returns it). */
-#define EKV_ABI_VERSION 3
+#define EKV_ABI_VERSION 4
 
 #ifdef __cplusplus
 extern "C" {
@@ -228,6 +228,32 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
                              float* out, float* tau, int32_t* support, float* delta,
                              int32_t* support_ref,
                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Bytes of device scratch that ekv_entmax_decode_noalloc holds per GPU. */
+#define EKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* ekv_entmax_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, computation, outputs
+ * and errors as ekv_entmax_decode; it calls no hipMalloc/hipFree and no
+ * allocating library routine.  Its scratch is a static device array of
+ * EKV_NOALLOC_SCRATCH_BYTES per GPU (one copy per device, held until the
+ * process ends, its address looked up on the first call on each device).
+ *   - A decode whose workspace need (as ekv_entmax_decode would report it)
+ *     exceeds EKV_NOALLOC_SCRATCH_BYTES returns EKV_ERR_WORKSPACE before
+ *     enqueuing anything.
+ *   - Every call on one GPU uses that GPU's one array: calls whose kernels
+ *     overlap on one GPU (different streams, or different host threads
+ *     without ordering) race on it and give undefined results.  Calls on one
+ *     stream are ordered and safe.  The kernels write every scratch byte
+ *     they read, so nothing needs to start at zero.                        */
+ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* page_table, const int32_t* seq_lens,
+                                     const int32_t* sel_pages, const int32_t* sel_count,
+                                     int32_t sel_stride, float alpha, const float* tau_ref,
+                                     float* out, float* tau, int32_t* support, float* delta,
+                                     int32_t* support_ref, void* stream);
 
 /* Message describing the last error returned on this thread ("" if none). */
 const char* ekv_last_error(void);

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ekv.h"
 #include "ekv_internal.h"
 
@@ -72,6 +74,50 @@ bool gauss_alpha_ok(float alpha) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Argument checks shared by ekv_entmax_decode and ekv_entmax_decode_noalloc
+// that do not involve the workspace; fills the workspace plan.
+ekv_status check_decode(const ekv_shape* shape, int sparse, int32_t sel_stride, const int32_t* sel_count,
+                        float alpha, const float* tau_ref, const float* delta, const int32_t* support_ref,
+                        ekv::Dims* d, ekv::DecodePlan* pl) {
+    ekv_status st = check_shape(shape, d);
+    if (st != EKV_OK) return st;
+    if (!(alpha >= 1.0f) || !(alpha < 1e6f)) return fail(EKV_ERR_INVALID_ARG, "alpha must be >= 1 (got %g)", alpha);
+    if (sparse && sel_stride < 1) return fail(EKV_ERR_INVALID_ARG, "sel_stride=%d < 1", sel_stride);
+    if (sparse && !sel_count) return fail(EKV_ERR_INVALID_ARG, "sel_count is required with sel_pages");
+    if (delta && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "delta needs tau_ref");
+    if (support_ref && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "support_ref needs tau_ref");
+    *pl = ekv::plan_decode(*d, sparse, sparse ? sel_stride : 0, alpha);
+    return EKV_OK;
+}
+
+// Scratch memory of ekv_entmax_decode_noalloc: one copy of this array per GPU
+// the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it names a stand-in, not
+// device memory): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept in g_scratch.
+constexpr size_t kNoallocScratchBytes = (size_t)EKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call per device; concurrent first calls store the same address).
+hipError_t scratch_ptr(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -190,16 +236,11 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
                              void* workspace,
                              size_t* workspace_bytes, void* stream) {
     ekv::Dims d;
-    ekv_status st = check_shape(shape, &d);
+    ekv::DecodePlan pl;
+    const int sparse = sel_pages != nullptr;
+    ekv_status st = check_decode(shape, sparse, sel_stride, sel_count, alpha, tau_ref, delta, support_ref, &d, &pl);
     if (st != EKV_OK) return st;
     if (!workspace_bytes) return fail(EKV_ERR_INVALID_ARG, "workspace_bytes is NULL");
-    if (!(alpha >= 1.0f) || !(alpha < 1e6f)) return fail(EKV_ERR_INVALID_ARG, "alpha must be >= 1 (got %g)", alpha);
-    const int sparse = sel_pages != nullptr;
-    if (sparse && sel_stride < 1) return fail(EKV_ERR_INVALID_ARG, "sel_stride=%d < 1", sel_stride);
-    if (sparse && !sel_count) return fail(EKV_ERR_INVALID_ARG, "sel_count is required with sel_pages");
-    if (delta && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "delta needs tau_ref");
-    if (support_ref && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "support_ref needs tau_ref");
-    const ekv::DecodePlan pl = ekv::plan_decode(d, sparse, sparse ? sel_stride : 0, alpha);
     if (!workspace) {
         *workspace_bytes = pl.bytes;
         return ok();
@@ -213,6 +254,32 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
                                          sel_stride, alpha, tau_ref, out, tau, support, delta, support_ref, (char*)workspace,
                                          (hipStream_t)stream),
                       "ekv_entmax_decode");
+}
+
+ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                                     const int32_t* sel_pages, const int32_t* sel_count, int32_t sel_stride,
+                                     float alpha, const float* tau_ref, float* out, float* tau, int32_t* support,
+                                     float* delta, int32_t* support_ref, void* stream) {
+    ekv::Dims d;
+    ekv::DecodePlan pl;
+    const int sparse = sel_pages != nullptr;
+    ekv_status st = check_decode(shape, sparse, sel_stride, sel_count, alpha, tau_ref, delta, support_ref, &d, &pl);
+    if (st != EKV_OK) return st;
+    if (pl.bytes > kNoallocScratchBytes)
+        return fail(EKV_ERR_WORKSPACE,
+                    "this decode needs %zu bytes of scratch, more than the %zu bytes the no-allocation entry "
+                    "point holds per GPU; use ekv_entmax_decode with a caller workspace",
+                    pl.bytes, kNoallocScratchBytes);
+    if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !tau)
+        return fail(EKV_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, seq_lens, out and tau are required");
+    void* ws = nullptr;
+    const hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_status(e, "ekv_entmax_decode_noalloc (scratch address)");
+    return hip_status(ekv::launch_decode(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count,
+                                         sel_stride, alpha, tau_ref, out, tau, support, delta, support_ref,
+                                         (char*)ws, (hipStream_t)stream),
+                      "ekv_entmax_decode_noalloc");
 }
 
 }  // extern "C"

@@ -26,7 +26,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 SEL_TOPK, SEL_GAUSS, SEL_SUPERSET = 0, 1, 2
 _STATUS = {0: "EKV_OK", 1: "EKV_ERR_INVALID_ARG", 2: "EKV_ERR_UNSUPPORTED", 3: "EKV_ERR_WORKSPACE", 4: "EKV_ERR_HIP"}
 SYMBOLS = ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
-           "ekv_last_error", "ekv_abi_version")
+           "ekv_entmax_decode_noalloc", "ekv_last_error", "ekv_abi_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20      # EKV_NOALLOC_SCRATCH_BYTES
 
 
 class EkvError(RuntimeError):
@@ -64,7 +65,10 @@ def load(path: str | None = None):
     lib.ekv_select.argtypes = [sp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
-    for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode"):
+    lib.ekv_entmax_decode_noalloc.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
+                                              _vp, _vp, _vp, _vp, _vp, _vp]
+    for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
+                 "ekv_entmax_decode_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ekv_last_error.restype = ctypes.c_char_p
     lib.ekv_last_error.argtypes = []
@@ -162,6 +166,16 @@ def entmax_decode(shape, q, k_cache, v_cache, page_table, seq_lens, sel_pages, s
                                     float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau), _ptr(support),
                                     _ptr(delta), _ptr(support_ref), _ptr(workspace), ctypes.byref(n),
                                     _stream(stream)))
+
+
+def entmax_decode_noalloc(shape, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count, sel_stride,
+                          alpha, out, tau, support=None, delta=None, tau_ref=None, support_ref=None, stream=None):
+    """ekv_entmax_decode_noalloc: the same decode on the library's static
+    per-GPU scratch (no workspace argument, no allocation)."""
+    _check(load().ekv_entmax_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(page_table), _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count),
+                                            int(sel_stride), float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau),
+                                            _ptr(support), _ptr(delta), _ptr(support_ref), _stream(stream)))
 
 
 # ------------------------------------------------------------- one step ----

@@ -37,7 +37,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ekv_abi_version() == 3
+    assert lib.ekv_abi_version() == 4
 
 
 def _shape(**kw):
@@ -169,3 +169,30 @@ def test_append_argument_checks(lib):
     st = lib.ekv_append_kv(a, 8, 8, 8, 1024, 8, 8, None, None, None, None, 1024, None)
     assert st == ekv.ERR_INVALID_ARG and b"alias" in lib.ekv_last_error()
     assert lib.ekv_append_kv(None, 8, 8, 8, 8, 8, 8, None, None, None, None, None, None) == ekv.ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_before_any_gpu_call(lib):
+    """ekv_entmax_decode_noalloc validates like ekv_entmax_decode and turns
+    away, on the host, a decode whose scratch need exceeds the static
+    per-GPU array (nothing is enqueued, so this runs without a GPU)."""
+    sh = _shape(batch=64, max_pages_per_seq=8192, num_phys_pages=8192)
+    need = ekv.decode_workspace_bytes(sh, False, 0, 1.5)          # full cache: logits of every token
+    assert need > ekv.NOALLOC_SCRATCH_BYTES
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(sh), 8, 8, 8, 8, 8, None, None, 0, 1.5, None, 8, 8, None,
+                                       None, None, None)
+    assert st == ekv.ERR_WORKSPACE
+    assert "scratch" in lib.ekv_last_error().decode()
+    small = _shape()
+    assert ekv.decode_workspace_bytes(small, True, 16, 1.5) <= ekv.NOALLOC_SCRATCH_BYTES
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, 8, 8, None,
+                                       None, None, None)
+    assert st == ekv.ERR_INVALID_ARG                       # alpha < 1
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, 8, 8, None,
+                                       None, None, None)
+    assert st == ekv.ERR_INVALID_ARG                       # sel_pages without sel_count
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), None, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None,
+                                       None, None, None)
+    assert st == ekv.ERR_INVALID_ARG                       # q missing
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None,
+                                       8, None, None)
+    assert st == ekv.ERR_INVALID_ARG                       # delta without tau_ref
