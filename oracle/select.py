@@ -20,7 +20,11 @@ Two policies ([EKV] section 4.3):
   reading R10 selects every page whose pooled margin
   t_{g,p} = max_{h in g} (mu_{h,p} - tau_hat_h/(alpha-1)) / sigma_{h,p}
   reaches -z (default z = 3), ranked by margin, capped, at least one page
-  (reading R11).  That rule is "parity unpinned": no worked example exists.
+  (reading R11).  The pages print no worked example of Eq. (21), so the
+  choice of this reading cannot be checked against them; its arithmetic is
+  pinned by hand-worked cases (tests/test_oracle_pins_by_hand.py) that a
+  sigma^2 divisor, a mean or minimum over heads, an undivided or dropped
+  threshold, a flipped sign or a strict comparison at -z would fail.
 """
 
 from __future__ import annotations
