@@ -255,6 +255,20 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q,
                                      float* out, float* tau, int32_t* support, float* delta,
                                      int32_t* support_ref, void* stream);
 
+/* Streaming-read probe (measurement only, not part of a decode step): reads
+ * `bytes` of device memory at `buf` (a positive multiple of 4096, 16-byte
+ * aligned) in 4 KiB chunks, in order (order == NULL) or in the order of the
+ * bytes/4096 device int32 chunk indices in `order` (an entry outside
+ * [0, bytes/4096) reads chunk 0).  It gives the read bandwidth the chip
+ * achieves for a linear stream and for 4 KiB pieces gathered through an
+ * index (the access pattern of page statistics and K tiles reached through
+ * a page table), against which the kernels' roofline fractions are read.
+ * `blocks` 256-thread blocks each keep `unroll` chunks (2, 4 or 8) in
+ * flight.  `sink` is one device uint32, written only if the folded data
+ * happens to equal a fixed constant (it keeps the loads live).           */
+ekv_status ekv_probe_read(const void* buf, size_t bytes, const int32_t* order, int32_t unroll,
+                          int32_t blocks, uint32_t* sink, void* stream);
+
 /* Message describing the last error returned on this thread ("" if none). */
 const char* ekv_last_error(void);
 

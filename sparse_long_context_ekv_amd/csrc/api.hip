@@ -282,4 +282,17 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q, cons
                       "ekv_entmax_decode_noalloc");
 }
 
+ekv_status ekv_probe_read(const void* buf, size_t bytes, const int32_t* order, int32_t unroll, int32_t blocks,
+                          uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(EKV_ERR_INVALID_ARG, "buf and sink are required");
+    if (bytes == 0 || bytes % 4096 != 0) return fail(EKV_ERR_INVALID_ARG, "bytes=%zu is not a positive multiple of 4096", bytes);
+    if (((uintptr_t)buf & 15) != 0) return fail(EKV_ERR_INVALID_ARG, "buf not 16-byte aligned");
+    if (bytes / 4096 > 0x7fffffffull) return fail(EKV_ERR_UNSUPPORTED, "more than 2^31 - 1 chunks");
+    if (unroll != 2 && unroll != 4 && unroll != 8) return fail(EKV_ERR_UNSUPPORTED, "unroll=%d not in {2,4,8}", unroll);
+    if (blocks < 1 || blocks > (1 << 20)) return fail(EKV_ERR_INVALID_ARG, "blocks=%d not in [1, 2^20]", blocks);
+    return hip_status(ekv::launch_probe_read(buf, (long)(bytes / 4096), order, unroll, blocks, sink,
+                                             (hipStream_t)stream),
+                      "ekv_probe_read");
+}
+
 }  // extern "C"

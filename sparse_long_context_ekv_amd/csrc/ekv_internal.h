@@ -79,4 +79,8 @@ hipError_t launch_decode_f32(const Dims& d, const DecodePlan& pl, const void* q,
                          float* delta, int32_t* supref, char* ws, hipStream_t s);
 
 
+// Streaming-read probe (probe.hip).
+hipError_t launch_probe_read(const void* buf, long n_chunks, const int32_t* order, int unroll, int blocks,
+                             uint32_t* sink, hipStream_t s);
+
 }  // namespace ekv

@@ -26,7 +26,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 SEL_TOPK, SEL_GAUSS, SEL_SUPERSET = 0, 1, 2
 _STATUS = {0: "EKV_OK", 1: "EKV_ERR_INVALID_ARG", 2: "EKV_ERR_UNSUPPORTED", 3: "EKV_ERR_WORKSPACE", 4: "EKV_ERR_HIP"}
 SYMBOLS = ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
-           "ekv_entmax_decode_noalloc", "ekv_last_error", "ekv_abi_version")
+           "ekv_entmax_decode_noalloc", "ekv_probe_read", "ekv_last_error", "ekv_abi_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20      # EKV_NOALLOC_SCRATCH_BYTES
 
 
@@ -67,8 +67,9 @@ def load(path: str | None = None):
                                       _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     lib.ekv_entmax_decode_noalloc.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.ekv_probe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]
     for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
-                 "ekv_entmax_decode_noalloc"):
+                 "ekv_entmax_decode_noalloc", "ekv_probe_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ekv_last_error.restype = ctypes.c_char_p
     lib.ekv_last_error.argtypes = []
@@ -176,6 +177,15 @@ def entmax_decode_noalloc(shape, q, k_cache, v_cache, page_table, seq_lens, sel_
                                             _ptr(page_table), _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count),
                                             int(sel_stride), float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau),
                                             _ptr(support), _ptr(delta), _ptr(support_ref), _stream(stream)))
+
+
+def probe_read(buf, order=None, unroll=8, blocks=2048, sink=None, stream=None):
+    """ekv_probe_read over the bytes of tensor `buf` (4 KiB chunks, linear or
+    in the chunk order of the int32 tensor `order`)."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(load().ekv_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(order), int(unroll), int(blocks),
+                                 _ptr(sink), _stream(stream)))
 
 
 # ------------------------------------------------------------- one step ----

@@ -196,3 +196,14 @@ def test_noalloc_decode_rejects_before_any_gpu_call(lib):
     st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None,
                                        8, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # delta without tau_ref
+
+
+def test_probe_read_validation(lib):
+    """The streaming-read probe rejects bad sizes and launch shapes on the host."""
+    sink = 64
+    assert lib.ekv_probe_read(4096, 4095, None, 8, 16, sink, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_probe_read(4096, 0, None, 8, 16, sink, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_probe_read(4100, 8192, None, 8, 16, sink, None) == ekv.ERR_INVALID_ARG    # misaligned
+    assert lib.ekv_probe_read(4096, 8192, None, 3, 16, sink, None) == ekv.ERR_UNSUPPORTED
+    assert lib.ekv_probe_read(4096, 8192, None, 8, 0, sink, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_probe_read(None, 8192, None, 8, 16, sink, None) == ekv.ERR_INVALID_ARG
