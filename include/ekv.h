@@ -59,7 +59,7 @@
 #include <stdint.h>
 
 /* ABI version of this header (ekv_abi_version() returns it). */
-#define EKV_ABI_VERSION 4
+#define EKV_ABI_VERSION 5
 
 #ifdef __cplusplus
 extern "C" {
@@ -207,6 +207,12 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  * sel_pages == NULL selects every page (full-cache decode); otherwise
  *   sel_pages [B][G][sel_stride] logical page indices (ascending not
  *   required) and sel_count [B][G] of them are used.
+ * tau_hint [B][HQ] fp32 (NULL ok; alpha > 1): a start for the threshold
+ *   iteration, in x units -- the selection's threshold estimate, which
+ *   [EKV] section 4.4 hands to decode with the selected pages (ekv_select's
+ *   EKV_SEL_GAUSS tau_hat).  It is used only where it lies strictly between
+ *   max(x) - 1 and max(x) over the head's candidate tokens; the threshold
+ *   found is the same, up to fp32 rounding, with or without it.
  * Outputs: out [B][HQ][D] fp32; tau [B][HQ] fp32 (x units; log-partition for
  *   alpha == 1); support [B][HQ] int32 nonzero count (NULL ok);
  *   delta [B][HQ] fp32 (NULL ok; needs tau_ref): dropped mass
@@ -224,9 +230,9 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
                              const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens,
                              const int32_t* sel_pages, const int32_t* sel_count,
-                             int32_t sel_stride, float alpha, const float* tau_ref,
-                             float* out, float* tau, int32_t* support, float* delta,
-                             int32_t* support_ref,
+                             int32_t sel_stride, float alpha, const float* tau_hint,
+                             const float* tau_ref, float* out, float* tau, int32_t* support,
+                             float* delta, int32_t* support_ref,
                              void* workspace, size_t* workspace_bytes, void* stream);
 
 /* Bytes of device scratch that ekv_entmax_decode_noalloc holds per GPU. */
@@ -251,9 +257,9 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q,
                                      const void* k_cache, const void* v_cache,
                                      const int32_t* page_table, const int32_t* seq_lens,
                                      const int32_t* sel_pages, const int32_t* sel_count,
-                                     int32_t sel_stride, float alpha, const float* tau_ref,
-                                     float* out, float* tau, int32_t* support, float* delta,
-                                     int32_t* support_ref, void* stream);
+                                     int32_t sel_stride, float alpha, const float* tau_hint,
+                                     const float* tau_ref, float* out, float* tau, int32_t* support,
+                                     float* delta, int32_t* support_ref, void* stream);
 
 /* Streaming-read probe (measurement only, not part of a decode step): reads
  * `bytes` of device memory at `buf` (a positive multiple of 4096, 16-byte

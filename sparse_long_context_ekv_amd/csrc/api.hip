@@ -231,7 +231,8 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
 
 ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens, const int32_t* sel_pages,
-                             const int32_t* sel_count, int32_t sel_stride, float alpha, const float* tau_ref,
+                             const int32_t* sel_count, int32_t sel_stride, float alpha, const float* tau_hint,
+                             const float* tau_ref,
                              float* out, float* tau, int32_t* support, float* delta, int32_t* support_ref,
                              void* workspace,
                              size_t* workspace_bytes, void* stream) {
@@ -250,17 +251,18 @@ ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q, const void* 
     if (((uintptr_t)workspace & 255) != 0) return fail(EKV_ERR_INVALID_ARG, "workspace not 256-byte aligned");
     if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !tau)
         return fail(EKV_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, seq_lens, out and tau are required");
+    const ekv::DecodeHeads io = {tau_hint, tau_ref, out, tau, support, delta, support_ref};
     return hip_status(ekv::launch_decode(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count,
-                                         sel_stride, alpha, tau_ref, out, tau, support, delta, support_ref, (char*)workspace,
-                                         (hipStream_t)stream),
+                                         sel_stride, alpha, io, (char*)workspace, (hipStream_t)stream),
                       "ekv_entmax_decode");
 }
 
 ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q, const void* k_cache,
                                      const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                                      const int32_t* sel_pages, const int32_t* sel_count, int32_t sel_stride,
-                                     float alpha, const float* tau_ref, float* out, float* tau, int32_t* support,
-                                     float* delta, int32_t* support_ref, void* stream) {
+                                     float alpha, const float* tau_hint, const float* tau_ref, float* out,
+                                     float* tau, int32_t* support, float* delta, int32_t* support_ref,
+                                     void* stream) {
     ekv::Dims d;
     ekv::DecodePlan pl;
     const int sparse = sel_pages != nullptr;
@@ -276,9 +278,9 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_shape* shape, const void* q, cons
     void* ws = nullptr;
     const hipError_t e = scratch_ptr(&ws);
     if (e != hipSuccess) return hip_status(e, "ekv_entmax_decode_noalloc (scratch address)");
+    const ekv::DecodeHeads io = {tau_hint, tau_ref, out, tau, support, delta, support_ref};
     return hip_status(ekv::launch_decode(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count,
-                                         sel_stride, alpha, tau_ref, out, tau, support, delta, support_ref,
-                                         (char*)ws, (hipStream_t)stream),
+                                         sel_stride, alpha, io, (char*)ws, (hipStream_t)stream),
                       "ekv_entmax_decode_noalloc");
 }
 

@@ -48,8 +48,7 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
 hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                         float alpha, const float* tau_ref, float* out, float* tau,
-                         int32_t* support, float* delta, int32_t* supref, char* ws, hipStream_t s) {
+                         float alpha, const DecodeHeads& io, char* ws, hipStream_t s) {
     int mode;
     float beta = 0.0f;
     if (alpha == 1.0f) {
@@ -60,7 +59,7 @@ hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, con
     }
     return (d.kv_bf16 ? launch_decode_bf16 : launch_decode_f32)(d, pl, q, k_cache, v_cache, page_table, seq_lens,
                                                                sel_pages, sel_count, sel_stride, alpha, mode, beta,
-                                                               tau_ref, out, tau, support, delta, supref, ws, s);
+                                                               io, ws, s);
 }
 
 }  // namespace ekv

@@ -183,18 +183,115 @@ __device__ __forceinline__ float powb(float d, int mode, float beta) {
     return mode == kModeBeta1 ? d : (mode == kModeBeta2 ? d * d : powf(d, beta));
 }
 
+// State of the threshold iteration of one head for beta >= 1, where
+// F(t) = sum_j [x_j - t]_+^beta is decreasing and G = F^(1/beta), the L^beta
+// norm of (x - t)_+, is convex, so that:
+//  * from a point left of the root (F >= 1) a Newton step on G rises and
+//    never passes the root;
+//  * from a point right of the root (F < 1) the Newton (tangent) step on G
+//    lands at or left of the root.
+// The iteration may therefore start anywhere in [max - 1, max) (e.g. at the
+// Gaussian threshold estimate of the full cache); it keeps the best point
+// known to lie left of the root (tl) and right of it (tr).  For beta = 1 and
+// 2 every step first tries the closed form on the current support
+// S = {x > t}: with d = x - t over S, s1 = sum d^beta, s0 = sum d^(beta-1),
+// k = |S|,
+//     beta = 1:  tau = t + (s1 - 1)/k,
+//     beta = 2:  tau = t + m - sqrt((1 - V)/k),  m = s0/k, V = s1 - s0 m
+//                (V the centred sum of squares of S, which must be <= 1),
+// and accepts it when it is consistent with S (min_S x > tau >= every other
+// candidate): the threshold is unique, so a consistent value is exact.
+struct TauIter {
+    float t, tl, tr, tau;
+    bool done;
+};
+
+__device__ __forceinline__ TauIter tau_iter_start(float lo, float xmax, float hint, bool empty) {
+    TauIter st;
+    st.t = (hint > lo && hint < xmax) ? hint : lo;   // a NaN or out-of-bracket hint starts at lo
+    st.tl = -INFINITY;
+    st.tr = INFINITY;
+    st.tau = lo;
+    st.done = empty;
+    return st;
+}
+
+// One step, given at st.t the sums over the candidates x > lo: s1, s0, k as
+// above, mn = min of the candidates above t, rest = max of those at or below.
+template <int MODE>
+__device__ __forceinline__ void tau_iter_step(TauIter& st, float lo, float beta, float s1, float s0, float k,
+                                              float mn, float rest) {
+    const float t = st.t;
+    if constexpr (MODE == kModeBeta1 || MODE == kModeBeta2) {
+        if (k > 0.0f) {
+            const float rk = hw_rcp(k);
+            float tcf;
+            if constexpr (MODE == kModeBeta1) {
+                tcf = t + (s1 - 1.0f) * rk;
+            } else {
+                const float m = s0 * rk;
+                const float v = fmaf(-s0, m, s1);
+                tcf = v <= 1.0f ? t + m - hw_sqrt((1.0f - v) * rk) : NAN;
+            }
+            if (mn > tcf && !(rest > tcf)) {
+                st.tau = tcf;
+                st.done = true;
+                return;
+            }
+        }
+    }
+    if (!(s1 > 0.0f) || !(s0 > 0.0f)) {
+        // nothing above t: a start at or above every candidate; restart at lo
+        if (t > lo) {
+            st.t = lo;
+        } else {
+            st.tau = t;
+            st.done = true;
+        }
+        return;
+    }
+    const float g = MODE == kModeBeta1 ? s1 : (MODE == kModeBeta2 ? hw_sqrt(s1) : hw_pow(s1, hw_rcp(beta)));
+    const float nt = t + (1.0f - hw_rcp(g)) * s1 * hw_rcp(s0);
+    if (s1 >= 1.0f) {                       // at or left of the root
+        st.tl = t;
+        if (!(nt > t)) {                    // no progress at fp32 resolution
+            st.tau = t;
+            st.done = true;
+        } else if (!(nt < st.tr)) {         // the root lies in [t, tr] and the step says it is at tr
+            st.tau = st.tr;
+            st.done = true;
+        } else {
+            st.t = nt;
+        }
+    } else {                                // right of the root: the tangent step lands at or left of it
+        st.tr = t;
+        const float nl = fmaxf(nt, fmaxf(lo, st.tl));
+        if (st.tl > -INFINITY || !(nl < t)) {
+            // a step from the left passed the root by rounding (the only way
+            // back to the right side), or no step is left: the tangent point,
+            // or the last left point if that is nearer, is within rounding of
+            // the root
+            st.tau = nl < t ? nl : t;
+            st.done = true;
+        } else {
+            st.t = nl;
+        }
+    }
+}
+
 static __global__ __launch_bounds__(256) void tau_kernel(
     const float* __restrict__ logits, const float* __restrict__ part1,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
-    int mode, float alpha, float beta, const float* __restrict__ tau_ref, float* __restrict__ tau_out,
-    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out,
-    const float* __restrict__ ccand, const int32_t* __restrict__ ccnt, int ncc) {
+    int mode, float alpha, float beta, const float* __restrict__ tau_hint, const float* __restrict__ tau_ref,
+    float* __restrict__ tau_out, int32_t* __restrict__ support_out, float* __restrict__ delta_out,
+    int32_t* __restrict__ supref_out, const float* __restrict__ ccand, const int32_t* __restrict__ ccnt, int ncc) {
     __shared__ float cand[kCandCap];
     __shared__ int coff[kCandMaxChunks + 1];
     __shared__ float red[8];
     __shared__ int wsum[8];
-    int phase = 0;
+    __shared__ float red5[2][4][5];
+    int phase = 0, p5 = 0;
     const int h = blockIdx.x, b = blockIdx.y;
     const int R = HQ / G;
     const int unit = b * G + h / R;
@@ -333,16 +430,64 @@ static __global__ __launch_bounds__(256) void tau_kernel(
         return r;
     };
 
+    // Three block sums (fixed order), a minimum and a maximum with one
+    // barrier (red5 alternates, as block_sum's buffer does).
+    auto block5 = [&](float v0, float v1, float v2, float vmin, float vmax, float* r) {
+        const float a0 = wave_sum(v0), a1 = wave_sum(v1), a2 = wave_sum(v2);
+        const float a3 = -wave_max(-vmin), a4 = wave_max(vmax);
+        const int wid = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            red5[p5][wid][0] = a0;
+            red5[p5][wid][1] = a1;
+            red5[p5][wid][2] = a2;
+            red5[p5][wid][3] = a3;
+            red5[p5][wid][4] = a4;
+        }
+        __syncthreads();
+        r[0] = r[1] = r[2] = 0.0f;
+        r[3] = INFINITY;
+        r[4] = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            r[0] += red5[p5][w2][0];
+            r[1] += red5[p5][w2][1];
+            r[2] += red5[p5][w2][2];
+            r[3] = fminf(r[3], red5[p5][w2][3]);
+            r[4] = fmaxf(r[4], red5[p5][w2][4]);
+        }
+        p5 ^= 1;
+    };
+
     float tau = lo;
     if (beta >= 1.0f) {
-        for (int it = 0; it < 100; ++it) {
-            const TauSums r = sums(tau, lo, true);
-            const float F = r.s1 - 1.0f;
-            if (!(F > 0.0f) || !(r.s0 > 0.0f)) break;
-            const float nt = tau + F / (beta * r.s0);
-            if (!(nt > tau)) break;
-            tau = nt;
+        // From max - 1, or from tau_hint when it lies in (max - 1, max); each
+        // step one pass and one barrier (see TauIter).  The state is
+        // block-uniform: every thread steps on the same block sums.
+        TauIter st = tau_iter_start(lo, a * mx, tau_hint ? tau_hint[oh] : NAN, false);
+        const int lim = in_lds ? ncand : nused;
+        for (int it = 0; it < 100 && !st.done; ++it) {
+            const float t = st.t;
+            float s1 = 0.0f, s0 = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
+            for (int i = threadIdx.x; i < lim; i += 256) {
+                const float x = in_lds ? cand[i] : a * lrow[i];
+                if (!(x > lo)) continue;
+                const float dd = x - t;
+                if (dd > 0.0f) {
+                    s1 += powb(dd, mode, beta);
+                    s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? dd : powf(dd, beta - 1.0f));
+                    kk += 1.0f;
+                    mn = fminf(mn, x);
+                } else {
+                    rest = fmaxf(rest, x);
+                }
+            }
+            float r[5];
+            block5(s1, s0, kk, mn, rest, r);
+            if (mode == kModeBeta1) tau_iter_step<kModeBeta1>(st, lo, beta, r[0], r[1], r[2], r[3], r[4]);
+            else if (mode == kModeBeta2) tau_iter_step<kModeBeta2>(st, lo, beta, r[0], r[1], r[2], r[3], r[4]);
+            else tau_iter_step<kModeGeneral>(st, lo, beta, r[0], r[1], r[2], r[3], r[4]);
         }
+        tau = st.done ? st.tau : st.t;
     } else {
         // beta < 1 (alpha > 2): the sum is not convex; bisect.
         float hi = a * mx - powf(C, 1.0f - alpha);
@@ -353,37 +498,6 @@ static __global__ __launch_bounds__(256) void tau_kernel(
             if (r.s1 - 1.0f >= 0.0f) l2 = mid; else hi = mid;
         }
         tau = 0.5f * (l2 + hi);
-    }
-
-    // Closed form on the support found (beta = 1 or 2), kept if consistent.
-    if (mode == kModeBeta1 || mode == kModeBeta2) {
-        float sx = 0.0f, k = 0.0f, mn = INFINITY, rest = -INFINITY;
-        const int lim = in_lds ? ncand : nused;
-        for (int i = threadIdx.x; i < lim; i += 256) {
-            const float x = in_lds ? cand[i] : a * lrow[i];
-            if (x > tau) { sx += x; k += 1.0f; mn = fminf(mn, x); }
-            else if (x > lo) rest = fmaxf(rest, x);
-        }
-        sx = block_sum<4>(sx, red, phase);
-        k = block_sum<4>(k, red, phase);
-        mn = -block_max<4>(-mn, red, phase);
-        rest = block_max<4>(rest, red, phase);
-        float tcf = NAN;
-        if (k > 0.0f) {
-            if (mode == kModeBeta1) {
-                tcf = (sx - 1.0f) / k;
-            } else {
-                const float mean = sx / k;
-                float v = 0.0f;
-                for (int i = threadIdx.x; i < lim; i += 256) {
-                    const float x = in_lds ? cand[i] : a * lrow[i];
-                    if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
-                }
-                v = block_sum<4>(v, red, phase);
-                if (v <= 1.0f) tcf = mean - sqrtf((1.0f - v) / k);
-            }
-        }
-        if (tcf == tcf && mn > tcf && !(rest > tcf)) tau = tcf;
     }
 
     // Support size and dropped mass with respect to tau_ref.
@@ -682,13 +796,14 @@ __device__ __forceinline__ float pw1(float d, float beta) {     // d^(beta-1), d
 //     slots into its own LDS list, lane by lane after one wave scan of
 //     per-lane counts (a fixed order, so results are reproducible); past CW
 //     candidates the wave keeps working on its registers;
-//  3. tau from sum [x - tau]_+^beta = 1 by Newton steps on F^(1/beta) from
-//     tau = max(x) - 1: for beta >= 1 this is the L^beta norm of (x - tau)_+,
-//     convex and decreasing, so the steps rise monotonically without passing
-//     the root (beta < 1: bisection).  Each iteration sums per wave, and the
-//     head's W partials are added in a fixed order after one block barrier
-//     (partials double-buffered); for beta in {1, 2} the closed form on the
-//     support found then gives tau exactly;
+//  3. tau from sum [x - tau]_+^beta = 1 (TauIter): from tau = max(x) - 1, or
+//     from the caller's tau_hint (the Gaussian selector's estimate, as the
+//     selection hands it to decode) when it lies in (max - 1, max); each step
+//     tries the closed form on the current support (beta in {1, 2}) and
+//     otherwise takes a Newton step on F^(1/beta), the L^beta norm of
+//     (x - tau)_+, convex and decreasing (beta < 1: bisection).  Each step
+//     sums per wave, and the head's W partials are combined in a fixed order
+//     after one block barrier (partials double-buffered);
 //  4. tau, the support size and the dropped mass w.r.t. tau_ref (tau_ref,
 //     the threshold over a superset of these tokens, is at least max(x) - 1,
 //     so only candidates contribute);
@@ -700,21 +815,26 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     const T* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, const float* __restrict__ logits,
-    int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_ref,
-    float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
-    float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
+    int G, int MP, int NP, float alpha, float beta, const float* __restrict__ tau_hint,
+    const float* __restrict__ tau_ref, float* __restrict__ out, float* __restrict__ tau_out,
+    int32_t* __restrict__ support_out, float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
     constexpr int NWV = R * W;                   // waves in the block
     constexpr int CH = D / kRow;
     constexpr int PVU = 4;                       // V rows per 16-lane row in flight
     constexpr int NPG = W * KPLW * 256 / kPage;  // selected pages per head at most
-    constexpr int CW = kCandLds / W;             // candidates per wave kept in LDS
+    // candidates per wave kept in LDS: room for twice a wave's even share of
+    // the head's kCandLds (a wave may hold more than its share), at most 512
+    // so that the block's LDS stays within 160 KiB
+    constexpr int CW = (2 * kCandLds / W) < 512 ? (2 * kCandLds / W) : 512;
     constexpr int PW = kPvList / W;              // support entries per wave per pass
     __shared__ float cand_x[NWV][CW + 64];       // + one dump slot per lane
     __shared__ int cand_s[NWV][CW + 64];
     __shared__ int pv_slot[NWV][PW + 64];
     __shared__ float pv_p[NWV][PW + 64];
     __shared__ int phys_of[NPG];
-    __shared__ float part[2][NWV][4];
+    __shared__ float part[2][NWV][5];
+    __shared__ int wave_nc[NWV];                 // candidates of each wave in LDS, -1 if not
+    __shared__ float sh_tau[R];
     __shared__ int flag[2][NWV];
     __shared__ float pvout[NWV][D];
     const int unit = blockIdx.x;
@@ -830,64 +950,168 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
                     if (xr[k][c] > lo) fn(xr[k][c], base + k * 256 + 4 * lane + c);
         }
     };
-    // Sum of the head's W wave partials (fixed order), after a barrier.  The
-    // partials alternate between part[0] and part[1]: a call writes the
-    // buffer that the call before the previous one read, and the previous
-    // call's barrier lies between those reads and this write.  Step 1 above
-    // read part[0] with no barrier after it, so the first call must write
-    // part[1] (pb starts at 0 and is flipped before the write).
+    // The head's W wave partials after a barrier: three sums (fixed order), a
+    // minimum and a maximum.  The partials alternate between part[0] and
+    // part[1]: a call writes the buffer that the call before the previous
+    // one read, and the previous call's barrier lies between those reads and
+    // this write.  Step 1 above read part[0] with no barrier after it, so the
+    // first call must write part[1] (pb starts at 0 and is flipped before the
+    // write).  `any` tells whether any wave of the block passed fl != 0.
     int pb = 0;
-    auto head_sums = [&](float v0, float v1, float v2, float v3, int fl, float* r, bool& any) {
+    auto head_sums = [&](float v0, float v1, float v2, float vmin, float vmax, int fl, float* r, bool& any) {
         pb ^= 1;
         if (lane == 0) {
             part[pb][wv][0] = v0;
             part[pb][wv][1] = v1;
             part[pb][wv][2] = v2;
-            part[pb][wv][3] = v3;
+            part[pb][wv][3] = vmin;
+            part[pb][wv][4] = vmax;
             flag[pb][wv] = fl;
         }
         __syncthreads();
-        r[0] = r[1] = r[2] = r[3] = 0.0f;
+        r[0] = r[1] = r[2] = 0.0f;
+        r[3] = INFINITY;
+        r[4] = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < W; ++w2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] += part[pb][j * W + w2][i];
+        for (int w2 = 0; w2 < W; ++w2) {
+            const float* pw = part[pb][j * W + w2];
+            r[0] += pw[0];
+            r[1] += pw[1];
+            r[2] += pw[2];
+            r[3] = fminf(r[3], pw[3]);
+            r[4] = fmaxf(r[4], pw[4]);
+        }
         any = false;
 #pragma unroll
         for (int v2 = 0; v2 < NWV; ++v2) any = any || flag[pb][v2] != 0;
     };
 
-    // 3. tau
+    // 3. tau.  Every step of the iteration is a pass over the head's
+    // candidates, a handful of reductions and scalar-like arithmetic that
+    // every wave of the head would repeat; with 16 waves on a CU that
+    // repeated work is what the iteration costs.  So when every wave's
+    // candidates are in LDS (the usual case), one wave per head gathers the
+    // head's candidates (at most kCandLds) into registers and iterates alone,
+    // with wave-level sums and no block barrier, and a single barrier hands
+    // tau to the head's other waves.  Otherwise every wave iterates on its
+    // own candidates and the head's partials meet after a barrier per step.
+    // Both start from max - 1, or from the caller's estimate (tau_hint, e.g.
+    // the Gaussian threshold estimate of the full cache) when it lies in
+    // (max - 1, max); see TauIter (beta < 1: bisection).
+    if (lane == 0) wave_nc[wv] = in_lds ? ncand : -1;
+    __syncthreads();
+    bool all_lds = true;                         // every wave in LDS, every head within kCandLds
+#pragma unroll
+    for (int j2 = 0; j2 < R; ++j2) {
+        int tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) {
+            const int c = wave_nc[j2 * W + w2];
+            all_lds = all_lds && c >= 0;
+            tot += c;
+        }
+        all_lds = all_lds && tot <= kCandLds;
+    }
+    const float hint = (tau_hint && !empty) ? tau_hint[oh] : NAN;
     float tau = lo;
-    if (MODE != kModeGeneral || beta >= 1.0f) {
-        bool active = !empty;
+    if (all_lds) {                                           // block-uniform
+        if (w == j % W) {                                    // the head's iterating wave
+            constexpr int NH = kCandLds / 64;
+            int off[W + 1];
+            off[0] = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < W; ++w2) off[w2 + 1] = off[w2] + wave_nc[j * W + w2];
+            const int nh = off[W];
+            float hx[NH];
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+                // element e of the concatenated lists: list w2, entry e - off[w2]
+                // (a select chain, so that no register array is indexed at run time)
+                const int e = lane + 64 * i;
+                int w2 = 0, base = 0;
+#pragma unroll
+                for (int u = 1; u < W; ++u) {
+                    const bool past = e >= off[u];
+                    w2 = past ? u : w2;
+                    base = past ? off[u] : base;
+                }
+                hx[i] = e < nh ? cand_x[j * W + w2][e - base] : -INFINITY;
+            }
+            // (guards, not breaks, so that the loops unroll and hx stays in registers)
+            auto each_h = [&](auto&& fn) {
+#pragma unroll
+                for (int i = 0; i < NH; ++i)
+                    if (i * 64 < nh && hx[i] > lo) fn(hx[i]);      // first test wave-uniform
+            };
+            if (MODE != kModeGeneral || beta >= 1.0f) {
+                TauIter st = tau_iter_start(lo, xmax, hint, empty);
+                for (int it = 0; it < 100 && !st.done; ++it) {   // wave-uniform
+                    const float t = st.t;                        // t >= lo
+                    float s1 = 0.0f, s0 = 0.0f, mn = INFINITY, rest = -INFINITY;
+                    int kk = 0;
+                    // Branch-free: selects instead of divergent paths per element
+                    // (entries past the list are -inf: not above t, not above lo).
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) {
+                        if (i * 64 >= nh) continue;              // wave-uniform
+                        const float x = hx[i];
+                        const float d = x - t;
+                        const bool in = d > 0.0f;
+                        const float dp = in ? d : 0.0f;
+                        s1 += in ? pw<MODE>(dp, beta) : 0.0f;
+                        s0 += in ? pw1<MODE>(dp, beta) : 0.0f;
+                        kk += in ? 1 : 0;
+                        mn = in ? fminf(mn, x) : mn;
+                        rest = (!in && x > lo) ? fmaxf(rest, x) : rest;
+                    }
+                    tau_iter_step<MODE>(st, lo, beta, wave_sum(s1), wave_sum(s0), (float)wave_isum(kk),
+                                        -wave_max(-mn), wave_max(rest));
+                }
+                tau = st.done ? st.tau : st.t;
+            } else {
+                float l2 = lo, hi = xmax - powf(nvalid, 1.0f - alpha);
+                for (int it = 0; it < 60 && !empty; ++it) {
+                    const float mid = 0.5f * (l2 + hi);
+                    float s1 = 0.0f;
+                    each_h([&](float x) {
+                        const float d = x - mid;
+                        if (d > 0.0f) s1 += pw<MODE>(d, beta);
+                    });
+                    if (wave_sum(s1) >= 1.0f) l2 = mid; else hi = mid;
+                }
+                tau = 0.5f * (l2 + hi);
+            }
+            if (lane == 0) sh_tau[j] = tau;
+        }
+        __syncthreads();
+        tau = sh_tau[j];
+    } else if (MODE != kModeGeneral || beta >= 1.0f) {
+        TauIter it_st = tau_iter_start(lo, xmax, hint, empty);
         for (int it = 0; it < 100; ++it) {
-            float s1 = 0.0f, s0 = 0.0f;
-            if (active)
+            float s1 = 0.0f, s0 = 0.0f, mn = INFINITY, rest = -INFINITY;
+            int kk = 0;
+            if (!it_st.done) {
+                const float t = it_st.t;
                 each_cand([&](float x, int) {
-                    const float d = x - tau;
+                    const float d = x - t;
                     if (d > 0.0f) {
                         s1 += pw<MODE>(d, beta);
                         s0 += pw1<MODE>(d, beta);
+                        ++kk;
+                        mn = fminf(mn, x);
+                    } else {
+                        rest = fmaxf(rest, x);
                     }
                 });
-            s1 = wave_sum(s1);
-            s0 = wave_sum(s0);
-            float r[4];
-            bool any;
-            head_sums(s1, s0, 0.0f, 0.0f, active ? 1 : 0, r, any);
-            if (!any) break;                                 // block-uniform
-            if (active) {
-                const float f = r[0], df = r[1];
-                if (!(f > 1.0f) || !(df > 0.0f)) {
-                    active = false;
-                } else {
-                    const float gr = MODE == kModeBeta1 ? f : (MODE == kModeBeta2 ? sqrtf(f) : powf(f, 1.0f / beta));
-                    const float nt = tau + (1.0f - 1.0f / gr) * f / df;
-                    if (!(nt > tau)) active = false; else tau = nt;
-                }
             }
+            float r[5];
+            bool any;
+            head_sums(wave_sum(s1), wave_sum(s0), (float)wave_isum(kk), -wave_max(-mn), wave_max(rest),
+                      it_st.done ? 0 : 1, r, any);
+            if (!any) break;                                 // block-uniform
+            if (!it_st.done) tau_iter_step<MODE>(it_st, lo, beta, r[0], r[1], r[2], r[3], r[4]);
         }
+        tau = it_st.done ? it_st.tau : it_st.t;
     } else {
         // beta < 1 (alpha > 2): bisection on [max - 1, max - n^(1-alpha)]
         float l2 = lo, hi = xmax - powf(nvalid, 1.0f - alpha);
@@ -899,44 +1123,12 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
                 if (d > 0.0f) s1 += pw<MODE>(d, beta);
             });
             s1 = wave_sum(s1);
-            float r[4];
+            float r[5];
             bool any;
-            head_sums(s1, 0.0f, 0.0f, 0.0f, 0, r, any);
+            head_sums(s1, 0.0f, 0.0f, 0.0f, 0.0f, 0, r, any);
             if (r[0] >= 1.0f) l2 = mid; else hi = mid;
         }
         tau = 0.5f * (l2 + hi);
-    }
-    // Closed form on the support found (beta in {1, 2}), kept if consistent.
-    if constexpr (MODE == kModeBeta1 || MODE == kModeBeta2) {
-        float sx = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
-        each_cand([&](float x, int) {
-            if (x > tau) { sx += x; kk += 1.0f; mn = fminf(mn, x); }
-            else rest = fmaxf(rest, x);
-        });
-        float r[4];
-        bool any;
-        head_sums(wave_sum(sx), wave_sum(kk), -wave_max(-mn), wave_max(rest), 0, r, any);
-        // r[2], r[3] (sums) are unused: the min and the max are taken over the waves
-        float mnh = INFINITY, resth = -INFINITY;
-#pragma unroll
-        for (int w2 = 0; w2 < W; ++w2) {
-            mnh = fminf(mnh, part[pb][j * W + w2][2]);
-            resth = fmaxf(resth, part[pb][j * W + w2][3]);
-        }
-        const float sxh = r[0], kkh = r[1];
-        float tcf = NAN;
-        if constexpr (MODE == kModeBeta1) {
-            if (kkh > 0.0f) tcf = (sxh - 1.0f) / kkh;
-        } else {
-            const float mean = kkh > 0.0f ? sxh / kkh : 0.0f;
-            float v = 0.0f;
-            each_cand([&](float x, int) {
-                if (x > tau) { const float dd = x - mean; v = fmaf(dd, dd, v); }
-            });
-            head_sums(wave_sum(v), 0.0f, 0.0f, 0.0f, 0, r, any);
-            if (kkh > 0.0f && r[0] <= 1.0f) tcf = mean - sqrtf((1.0f - r[0]) / kkh);
-        }
-        if (tcf == tcf && mnh > tcf && !(resth > tcf)) tau = tcf;
     }
 
     // 4. support size and dropped mass with respect to tau_ref
@@ -955,10 +1147,10 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
     const int sinc = wave_incl_scan(ns);
     const int nsw = __builtin_amdgcn_readlane(sinc, 63);      // this wave's support
     {
-        float r[4];
+        float r[5];
         bool any;
-        head_sums((float)nsw, want_ref ? wave_sum(kept) : 0.0f, want_ref ? (float)wave_isum(nref) : 0.0f, 0.0f, 0,
-                  r, any);
+        head_sums((float)nsw, want_ref ? wave_sum(kept) : 0.0f, want_ref ? (float)wave_isum(nref) : 0.0f, 0.0f, 0.0f,
+                  0, r, any);
         if (w == 0 && lane == 0) {
             tau_out[oh] = empty ? -INFINITY : tau;
             if (support_out) support_out[oh] = empty ? 0 : (int32_t)r[0];
@@ -1039,8 +1231,7 @@ __global__ __launch_bounds__(64 * R * W) void sparse_tau_pv_kernel(
 template <typename T, int D, int R, int MODE>
 static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_cache, const int32_t* pt,
                             const int32_t* sl, const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                            float alpha, float beta, const float* logits, const float* tau_ref, float* out,
-                            float* tau, int32_t* support, float* delta, int32_t* supref, hipStream_t s) {
+                            float alpha, float beta, const float* logits, const DecodeHeads& io, hipStream_t s) {
     const int units = d.B * d.G;
     // KPL float4 of logits per lane in all; W = 16 / R waves per head, at most KPL.
     constexpr int WMAX = 16 / R;
@@ -1049,7 +1240,7 @@ static hipError_t run_fused(const Dims& d, const DecodePlan& pl, const void* v_c
         constexpr int W = WMAX < KPL ? WMAX : KPL;                                                          \
         sparse_tau_pv_kernel<T, D, R, W, KPL / W, MODE><<<dim3(units), dim3(64 * R * W), 0, s>>>(           \
             (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, d.G, d.MP, d.NP, alpha, beta, \
-            tau_ref, out, tau, support, delta, supref);                                                     \
+            io.tau_hint, io.tau_ref, io.out, io.tau, io.support, io.delta, io.supref);                      \
         return hipGetLastError();                                                                           \
     }
     if (pl.nslot <= 256) EKV_FUSED(1)
@@ -1064,8 +1255,7 @@ template <typename T, int D, int R>
 static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                              const void* v_cache, const int32_t* pt, const int32_t* sl,
                              const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                             float alpha, int mode, float beta, const float* tau_ref, float* out,
-                             float* tau, int32_t* support, float* delta, int32_t* supref, char* ws,
+                             float alpha, int mode, float beta, const DecodeHeads& io, char* ws,
                              hipStream_t s) {
     float* logits = (float*)(ws + pl.off_logits);
     float* part1 = (float*)(ws + pl.off_part1);
@@ -1081,14 +1271,13 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         switch (mode) {
             case kModeBeta1:
                 return run_fused<T, D, R, kModeBeta1>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
+                                                      alpha, beta, logits, io, s);
             case kModeBeta2:
                 return run_fused<T, D, R, kModeBeta2>(d, pl, v_cache, pt, sl, sel_pages, sel_count, sel_stride,
-                                                      alpha, beta, logits, tau_ref, out, tau, support, delta, supref, s);
+                                                      alpha, beta, logits, io, s);
             default:
                 return run_fused<T, D, R, kModeGeneral>(d, pl, v_cache, pt, sl, sel_pages, sel_count,
-                                                        sel_stride, alpha, beta, logits, tau_ref, out, tau,
-                                                        support, delta, supref, s);
+                                                        sel_stride, alpha, beta, logits, io, s);
         }
     }
     logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
@@ -1109,15 +1298,16 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
     }
     tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
                                                      d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
-                                                     tau_ref, tau, support, delta, supref, ccand, ccnt, pl.ncc);
+                                                     io.tau_hint, io.tau_ref, io.tau, io.support, io.delta,
+                                                     io.supref, ccand, ccnt, pl.ncc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(
-        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, tau, d.G, d.MP, d.NP,
+        (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, logits, io.tau, d.G, d.MP, d.NP,
         pl.nslot, pl.spb, pl.nchunk3, mode, alpha, beta, part3);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    reduce_kernel<<<dim3(d.HQ, d.B), dim3(kReduceThreads), 0, s>>>(part3, d.HQ, D, pl.nchunk3, out);
+    reduce_kernel<<<dim3(d.HQ, d.B), dim3(kReduceThreads), 0, s>>>(part3, d.HQ, D, pl.nchunk3, io.out);
     return hipGetLastError();
 }
 
@@ -1127,13 +1317,11 @@ template <typename T>
 static hipError_t launch_decode_typed(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                                       const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                                      float alpha, int mode, float beta, const float* tau_ref, float* out,
-                                      float* tau, int32_t* support, float* delta, int32_t* supref, char* ws,
+                                      float alpha, int mode, float beta, const DecodeHeads& io, char* ws,
                                       hipStream_t s) {
 #define EKV_DEC(RR, DD)                                                                          \
     return run_decode<T, DD, RR>(d, pl, q, k_cache, v_cache, page_table, seq_lens, sel_pages,    \
-                                 sel_count, sel_stride, alpha, mode, beta, tau_ref, out, tau,     \
-                                 support, delta, supref, ws, s)
+                                 sel_count, sel_stride, alpha, mode, beta, io, ws, s)
 #define EKV_RSW(DD)                             \
     switch (d.R) {                              \
         case 1: EKV_DEC(1, DD);                 \

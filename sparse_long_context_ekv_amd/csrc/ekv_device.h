@@ -113,6 +113,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// ---------------------------------------------------- hardware math ----
+// Single-instruction approximations (about 1 ulp) for the arithmetic of
+// iteration steps, where rounding only changes how a step lands and never
+// the value the iteration converges to: the IEEE-exact division, sqrtf and
+// logf expand to long dependent instruction chains, which a one-wave
+// iteration pays on every step.
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_pow(float x, float y) { return hw_exp2(y * hw_log2(x)); }   // x > 0
+
 // ------------------------------------------------------- cross-lane ops ----
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

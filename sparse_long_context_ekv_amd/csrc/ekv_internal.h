@@ -59,24 +59,34 @@ struct DecodePlan {
     size_t off_logits, off_part1, off_part3, off_cand, off_ccnt, bytes;
 };
 DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha);
+
+// Per-(sequence, head) inputs and outputs of one decode, each [B][HQ]
+// (out [B][HQ][D]); the optional ones may be NULL.
+struct DecodeHeads {
+    const float* tau_hint;   // start of the threshold iteration (x units), or NULL
+    const float* tau_ref;    // threshold of the reference distribution (delta, supref), or NULL
+    float* out;
+    float* tau;
+    int32_t* support;
+    float* delta;
+    int32_t* supref;
+};
+
 hipError_t launch_decode(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel_pages, const int32_t* sel_count, int sel_stride,
-                         float alpha, const float* tau_ref, float* out, float* tau,
-                         int32_t* support, float* delta, int32_t* supref, char* ws, hipStream_t s);
+                         float alpha, const DecodeHeads& io, char* ws, hipStream_t s);
 
 // Per-dtype decode launches (decode_bf16.hip, decode_f32.hip); mode is the
 // entmax mode of decode_kernels.h and beta = 1/(alpha-1).
 hipError_t launch_decode_bf16(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
-                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
-                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
-                         int mode, float beta, const float* tau_ref, float* out, float* tau, int32_t* support,
-                         float* delta, int32_t* supref, char* ws, hipStream_t s);
+                              const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                              const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
+                              int mode, float beta, const DecodeHeads& io, char* ws, hipStream_t s);
 hipError_t launch_decode_f32(const Dims& d, const DecodePlan& pl, const void* q, const void* k_cache,
-                         const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
-                         const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
-                         int mode, float beta, const float* tau_ref, float* out, float* tau, int32_t* support,
-                         float* delta, int32_t* supref, char* ws, hipStream_t s);
+                             const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                             const int32_t* sel_pages, const int32_t* sel_count, int sel_stride, float alpha,
+                             int mode, float beta, const DecodeHeads& io, char* ws, hipStream_t s);
 
 
 // Streaming-read probe (probe.hip).

@@ -168,21 +168,24 @@ __device__ float gauss_tau_solve(const float2* __restrict__ src, const float* __
         float step_t = NAN;
         bool pure = false;                                      // an unmodified Halley / Newton step
         if (d1 > 0.0f && f > 0.0f) {
-            const float L = logf(f);
-            const float dL = -fb * d1 / f;                      // d log F / d tau
-            step_t = -L / dL;
+            // step arithmetic in single-instruction approximations (hw_*): it
+            // decides where a step lands, not the root F(t) = 1 converges to
+            const float rf = hw_rcp(f);
+            const float L = hw_log2(f) * 0.69314718055994531f;  // log F
+            const float dL = -fb * d1 * rf;                     // d log F / d tau
+            step_t = -L * hw_rcp(dL);
             pure = BETA == 1;
             if constexpr (BETA >= 2) {
-                const float d2L = fb * (fb - 1.0f) * d2 / f - dL * dL;
+                const float d2L = fb * (fb - 1.0f) * d2 * rf - dL * dL;
                 const float den = 2.0f * dL * dL - L * d2L;
                 if (den > 0.0f) {
-                    step_t = -2.0f * L * dL / den;
+                    step_t = -2.0f * L * dL * hw_rcp(den);
                     pure = true;
                 }
             }
             if (f > 1.0f) {
-                const float gr = BETA == 1 ? f : (BETA == 2 ? sqrtf(f) : cbrtf(f));
-                const float cap = 4.0f * (1.0f - 1.0f / gr) * f / d1;
+                const float gr = BETA == 1 ? f : (BETA == 2 ? hw_sqrt(f) : hw_exp2(hw_log2(f) * (1.0f / 3.0f)));
+                const float cap = 4.0f * (1.0f - hw_rcp(gr)) * f * hw_rcp(d1);
                 if (cap < step_t) {
                     step_t = cap;
                     pure = false;

@@ -63,9 +63,9 @@ def load(path: str | None = None):
     lib.ekv_append_kv.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_score_pages.argtypes = [sp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_select.argtypes = [sp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
-    lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
+    lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
-    lib.ekv_entmax_decode_noalloc.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp,
+    lib.ekv_entmax_decode_noalloc.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_probe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]
     for name in ("ekv_build_page_stats", "ekv_append_kv", "ekv_score_pages", "ekv_select", "ekv_entmax_decode",
@@ -154,28 +154,31 @@ def decode_workspace_bytes(shape, sparse: bool, sel_stride: int, alpha: float = 
     n = ctypes.c_size_t(0)
     dummy = 1 if sparse else None
     _check(load().ekv_entmax_decode(ctypes.byref(shape), None, None, None, None, None, dummy, dummy,
-                                    int(sel_stride), float(alpha), None, None, None, None, None, None, None,
+                                    int(sel_stride), float(alpha), None, None, None, None, None, None, None, None,
                                     ctypes.byref(n), None))
     return n.value
 
 
 def entmax_decode(shape, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count, sel_stride, alpha,
-                  out, tau, workspace, support=None, delta=None, tau_ref=None, support_ref=None, stream=None):
+                  out, tau, workspace, support=None, delta=None, tau_ref=None, support_ref=None, tau_hint=None,
+                  stream=None):
     n = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check(load().ekv_entmax_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                     _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count), int(sel_stride),
-                                    float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau), _ptr(support),
+                                    float(alpha), _ptr(tau_hint), _ptr(tau_ref), _ptr(out), _ptr(tau), _ptr(support),
                                     _ptr(delta), _ptr(support_ref), _ptr(workspace), ctypes.byref(n),
                                     _stream(stream)))
 
 
 def entmax_decode_noalloc(shape, q, k_cache, v_cache, page_table, seq_lens, sel_pages, sel_count, sel_stride,
-                          alpha, out, tau, support=None, delta=None, tau_ref=None, support_ref=None, stream=None):
+                          alpha, out, tau, support=None, delta=None, tau_ref=None, support_ref=None, tau_hint=None,
+                          stream=None):
     """ekv_entmax_decode_noalloc: the same decode on the library's static
     per-GPU scratch (no workspace argument, no allocation)."""
     _check(load().ekv_entmax_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                             _ptr(page_table), _ptr(seq_lens), _ptr(sel_pages), _ptr(sel_count),
-                                            int(sel_stride), float(alpha), _ptr(tau_ref), _ptr(out), _ptr(tau),
+                                            int(sel_stride), float(alpha), _ptr(tau_hint), _ptr(tau_ref), _ptr(out),
+                                            _ptr(tau),
                                             _ptr(support), _ptr(delta), _ptr(support_ref), _stream(stream)))
 
 
@@ -216,10 +219,13 @@ class Decoder:
     number of qualifying pages the result is exact."""
 
     def __init__(self, wl, selector: str, alpha: float, budget_pages: int, z: float = 3.0,
-                 stat_dtype: str = "f32", first_pages: int = 8):
+                 stat_dtype: str = "f32", first_pages: int = 8, tau_hint: bool = True):
         c = wl.cfg
         dev = wl.k_cache.device
         self.wl = wl
+        # Gaussian selector: hand its threshold estimate to decode as the start
+        # of the threshold iteration, with the selected pages.
+        self.use_hint = bool(tau_hint)
         self.superset = selector == "superset"
         self.selector = SEL_GAUSS if selector == "gauss" else SEL_TOPK
         self.alpha = float(alpha)
@@ -291,9 +297,10 @@ class Decoder:
 
     def decode(self, stream=None, tau_ref=None, delta=None, support_ref=None):
         wl, b = self.wl, self.buf
+        hint = b.tau_hat if (self.use_hint and self.selector == SEL_GAUSS and not self.superset) else None
         entmax_decode(self.shape, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, b.sel_pages,
                       b.sel_count, self.budget, self.alpha, b.out, b.tau, b.ws_decode, support=b.support,
-                      delta=delta, tau_ref=tau_ref, support_ref=support_ref, stream=stream)
+                      delta=delta, tau_ref=tau_ref, support_ref=support_ref, tau_hint=hint, stream=stream)
 
     def step(self, stream=None):
         self.score(stream)

@@ -37,7 +37,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ekv_abi_version() == 4
+    assert lib.ekv_abi_version() == 5
 
 
 def _shape(**kw):
@@ -60,7 +60,7 @@ def test_shape_validation(lib, kw, status):
     sh = _shape(**kw)
     sh.page_size = page_size
     n = ctypes.c_size_t(0)
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), None, None, None, None, None, None, None, 0, 1.5, None,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), None, None, None, None, None, None, None, 0, 1.5, None, None,
                                None, None, None, None, None, None, ctypes.byref(n), None)
     assert st == status
     assert lib.ekv_last_error().decode() != ""
@@ -137,23 +137,23 @@ def test_decode_workspace_query_and_checks(lib):
     assert 0 < sparse < full
     assert ekv.decode_workspace_bytes(sh, True, 16) == sparse
     n = ctypes.c_size_t(sparse - 1)
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, None, None, 256,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None, None, None, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_WORKSPACE
     n = ctypes.c_size_t(sparse)
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, 8, None, 256,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None, 8, None, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # delta without tau_ref
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, None, 8, 256,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None, None, 8, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # support_ref without tau_ref
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, 8, 8, None, None, None, 256,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, None, 8, 8, None, None, None, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # alpha < 1
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None, None, None, 300,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None, None, None, 300,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # misaligned workspace
-    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, 8, 8, None, None, None, 256,
+    st = lib.ekv_entmax_decode(ctypes.byref(sh), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, None, 8, 8, None, None, None, 256,
                                ctypes.byref(n), None)
     assert st == ekv.ERR_INVALID_ARG                       # sel_pages without sel_count
 
@@ -178,22 +178,22 @@ def test_noalloc_decode_rejects_before_any_gpu_call(lib):
     sh = _shape(batch=64, max_pages_per_seq=8192, num_phys_pages=8192)
     need = ekv.decode_workspace_bytes(sh, False, 0, 1.5)          # full cache: logits of every token
     assert need > ekv.NOALLOC_SCRATCH_BYTES
-    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(sh), 8, 8, 8, 8, 8, None, None, 0, 1.5, None, 8, 8, None,
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(sh), 8, 8, 8, 8, 8, None, None, 0, 1.5, None, None, 8, 8, None,
                                        None, None, None)
     assert st == ekv.ERR_WORKSPACE
     assert "scratch" in lib.ekv_last_error().decode()
     small = _shape()
     assert ekv.decode_workspace_bytes(small, True, 16, 1.5) <= ekv.NOALLOC_SCRATCH_BYTES
-    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, 8, 8, None,
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 0.5, None, None, 8, 8, None,
                                        None, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # alpha < 1
-    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, 8, 8, None,
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, None, 16, 1.5, None, None, 8, 8, None,
                                        None, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # sel_pages without sel_count
-    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), None, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None,
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), None, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None,
                                        None, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # q missing
-    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, 8, 8, None,
+    st = lib.ekv_entmax_decode_noalloc(ctypes.byref(small), 8, 8, 8, 8, 8, 8, 8, 16, 1.5, None, None, 8, 8, None,
                                        8, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # delta without tau_ref
 

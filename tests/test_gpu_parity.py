@@ -341,7 +341,7 @@ def _oracle_sel_tensor(sels, B, G, budget):
     return t.cuda(), cnt.cuda()
 
 
-def _run_decode(wl, alpha, sel=None, cnt=None, stride=0, tau_ref=None):
+def _run_decode(wl, alpha, sel=None, cnt=None, stride=0, tau_ref=None, tau_hint=None):
     c = wl.cfg
     sh = _shape(wl)
     out = torch.empty(c.batch, c.num_q_heads, c.head_dim, device="cuda")
@@ -351,7 +351,7 @@ def _run_decode(wl, alpha, sel=None, cnt=None, stride=0, tau_ref=None):
     supref = torch.empty_like(sup) if tau_ref is not None else None
     ws = torch.empty(ekv.decode_workspace_bytes(sh, sel is not None, stride, alpha), dtype=torch.uint8, device="cuda")
     ekv.entmax_decode(sh, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, sel, cnt, stride, alpha,
-                      out, tau, ws, support=sup, delta=delta, tau_ref=tau_ref, support_ref=supref)
+                      out, tau, ws, support=sup, delta=delta, tau_ref=tau_ref, support_ref=supref, tau_hint=tau_hint)
     H.sync()
     return out, tau, sup, delta, supref
 
@@ -508,3 +508,86 @@ def test_physical_placement_invariance():
     H.sync()
     assert torch.equal(dec.buf.out, dec2.buf.out)
     assert torch.equal(dec.buf.sel_pages, dec2.buf.sel_pages)
+
+
+@pytest.mark.parametrize("name,alpha", [("llama-ragged", 1.5), ("llama-ragged", 2.0), ("llama-ragged", 4.0 / 3.0),
+                                        ("llama-ragged-wide", 1.5), ("llama-ragged-wide", 2.0),
+                                        ("llama-ragged-wide", 4.0 / 3.0)])
+def test_decode_threshold_hint(name, alpha):
+    """Decode with a start for the threshold iteration (the hand-off of the
+    selection's threshold estimate to decode, "EntmaxKV" section 4.4): hints
+    left of the root, at it, right of it, at and past the largest score,
+    +-inf and NaN all give the oracle's threshold, support and output on the
+    selected tokens.  "llama-ragged-wide" (300 pages) takes the general path."""
+    wl = workload("llama-ragged")
+    c = wl.cfg
+    budget = 300 if name == "llama-ragged-wide" else c.budget_pages
+    sels = []
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sels.append(oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", alpha, budget)["sel"])
+    sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, budget)
+    ref = []
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        ref.append(oracle.decode.sparse_decode_groups(q, K, V, n, P, sels[b], alpha))
+    # per-head x range over the selected tokens, from the oracle
+    r = c.num_q_heads // c.num_kv_groups
+    xmax = torch.zeros(c.batch, c.num_q_heads, dtype=torch.float64)
+    tau_or = torch.zeros(c.batch, c.num_q_heads, dtype=torch.float64)
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        for h in range(c.num_q_heads):
+            toks = ref[b]["tokens_per_group"][h // r]
+            s_h = oracle.paged.token_scores(q[h:h + 1], K[:, h // r:h // r + 1, :], toks)[0]
+            xmax[b, h] = (alpha - 1.0) * s_h.max()
+            tau_or[b, h] = ref[b]["tau"][h]
+    hints = {
+        "left": 0.5 * (xmax - 1.0 + tau_or), "root": tau_or, "right": 0.5 * (tau_or + xmax),
+        "near_max": xmax - 1e-3, "max": xmax, "past_max": xmax + 5.0, "+inf": torch.full_like(xmax, float("inf")),
+        "-inf": torch.full_like(xmax, -float("inf")), "nan": torch.full_like(xmax, float("nan")),
+    }
+    base_out, base_tau, base_sup, _, _ = _run_decode(wl, alpha, sel, cnt, budget)
+    for hname, hv in hints.items():
+        print(f"[case] {name} alpha={alpha} hint={hname}", flush=True)
+        out, tau, sup, _, _ = _run_decode(wl, alpha, sel, cnt, budget, tau_hint=hv.float().cuda())
+        for b in range(c.batch):
+            assert np.abs(H.to_np(out[b]) - ref[b]["out"]).max() <= H.OUT_ATOL, (hname, b)
+            for h in range(c.num_q_heads):
+                assert H.tau_close(float(tau[b, h]), ref[b]["tau"][h]), (hname, b, h, float(tau[b, h]), ref[b]["tau"][h])
+        # the same threshold as without a hint, up to fp32 rounding
+        np.testing.assert_allclose(H.to_np(tau), H.to_np(base_tau), rtol=2e-6, atol=2e-6)
+        np.testing.assert_allclose(H.to_np(out), H.to_np(base_out), rtol=0, atol=2e-5)
+        assert int((sup - base_sup).abs().max()) <= 1
+
+
+@pytest.mark.parametrize("alpha", [4.0 / 3.0, 1.5, 2.0])
+def test_gaussian_step_with_threshold_hint(alpha):
+    """The Gaussian-selector step as bench times it: decode starts from the
+    selection's threshold estimate tau_hat; output and threshold against the
+    oracle's decode on the GPU's selection, and equal (to rounding) to the
+    same decode started without the estimate."""
+    wl = workload("gauss-ragged")
+    c = wl.cfg
+    cap = 64
+    dec = ekv.Decoder(wl, "gauss", alpha, cap, z=c.z)
+    dec.build_stats()
+    dec.step()
+    H.sync()
+    out_h, tau_h = dec.buf.out.clone(), dec.buf.tau.clone()
+    nohint = ekv.Decoder(wl, "gauss", alpha, cap, z=c.z, tau_hint=False)
+    nohint.stats = dec.stats
+    nohint.score()
+    nohint.select()
+    nohint.decode()
+    H.sync()
+    assert torch.equal(nohint.buf.sel_pages, dec.buf.sel_pages)
+    np.testing.assert_allclose(H.to_np(tau_h), H.to_np(nohint.buf.tau), rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(H.to_np(out_h), H.to_np(nohint.buf.out), rtol=0, atol=2e-5)
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sels = [dec.buf.sel_pages[b, g, :int(dec.buf.sel_count[b, g])].cpu().numpy() for g in range(c.num_kv_groups)]
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, sels, alpha)
+        assert np.abs(H.to_np(out_h[b]) - sp["out"]).max() <= H.OUT_ATOL
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau_h[b, h]), sp["tau"][h]), (b, h)
