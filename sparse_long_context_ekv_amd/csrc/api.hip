@@ -88,6 +88,9 @@ ekv_status check_decode(const ekv_shape* shape, int sparse, int32_t sel_stride, 
     if (delta && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "delta needs tau_ref");
     if (support_ref && !tau_ref) return fail(EKV_ERR_INVALID_ARG, "support_ref needs tau_ref");
     *pl = ekv::plan_decode(*d, sparse, sparse ? sel_stride : 0, alpha);
+    if (pl->too_long)
+        return fail(EKV_ERR_UNSUPPORTED, "rows of %d pages are longer than the decode is built for",
+                    sparse ? sel_stride : d->MP);
     return EKV_OK;
 }
 

@@ -9,38 +9,53 @@ namespace ekv {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
-    DecodePlan pl;
+    DecodePlan pl = {};
     pl.sparse = sparse;
     const int maxp = sparse ? sel_stride : d.MP;
     pl.nslot = maxp * kPage;
     pl.fused = sparse && alpha > 1.0f && pl.nslot <= kFusedMaxSlots;
+    pl.stream = !pl.fused && alpha > 1.0f;
+    const size_t bh = (size_t)d.B * d.HQ;
     pl.lg_ppb = sparse ? 3 : 5;
     pl.ppb = 1 << pl.lg_ppb;
     pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
     if (pl.nchunk1 < 1) pl.nchunk1 = 1;
-    pl.spb = sparse ? 256 : 4096;
-    pl.nchunk3 = (pl.nslot + pl.spb - 1) / pl.spb;
-    if (pl.nchunk3 < 1) pl.nchunk3 = 1;
-    const size_t bh = (size_t)d.B * d.HQ;
-    pl.off_logits = 0;
-    pl.off_part1 = align256(bh * pl.nslot * sizeof(float));
-    pl.ncc = 0;
-    pl.off_cand = pl.off_ccnt = 0;
     if (pl.fused) {
-        pl.off_part3 = pl.off_part1;
-        pl.bytes = pl.off_part1;
+        // selected logits [B][HQ][nslot]
+        pl.off_logits = 0;
+        pl.bytes = align256(bh * pl.nslot * sizeof(float));
+    } else if (pl.stream) {
+        // per (b, h, chunk): candidate list (x, slot), count, max; per (b, h):
+        // support list (p, slot), its count, kSupSplit partial outputs
+        // Chunks per block: about kStreamBlocks blocks in all, at most
+        // kStreamMaxChunks chunks per block; each block keeps up to 4 lists
+        // per head (one per wave on bf16 keys), kStreamMaxLists per (b, h).
+        const long nchunk = maxp > 0 ? (maxp + kStreamPpb - 1) / kStreamPpb : 1;
+        const long units = (long)d.B * d.G;
+        long cpb = (nchunk * units + kStreamBlocks - 1) / kStreamBlocks;
+        if (cpb < 1) cpb = 1;
+        if (cpb > kStreamMaxChunks) cpb = kStreamMaxChunks;
+        pl.cpb_s = (int)cpb;
+        pl.nsplit_s = (int)((nchunk + cpb - 1) / cpb);
+        // rows past kStreamMaxLists / 4 * kStreamMaxChunks chunks (16M tokens) are not built
+        pl.too_long = 4L * pl.nsplit_s > kStreamMaxLists;
+        const size_t rows = bh * pl.nsplit_s * 4;              // list counts and maxima
+        pl.off_cands = 0;
+        pl.off_ccount = pl.off_cands + align256(bh * pl.nsplit_s * pl.cpb_s * kStreamSlots * sizeof(float2));
+        pl.off_cmax = pl.off_ccount + align256(rows * sizeof(int32_t));
+        pl.off_sup = pl.off_cmax + align256(rows * sizeof(float));
+        pl.off_supcnt = pl.off_sup + align256(bh * pl.nslot * sizeof(float2));
+        pl.off_part3 = pl.off_supcnt + align256(bh * sizeof(int32_t));
+        pl.bytes = pl.off_part3 + align256(bh * kSupSplit * d.D * sizeof(float));
     } else {
+        // softmax: logits, chunk partials (max, sum exp, count), PV partials
+        pl.spb = sparse ? 256 : 4096;
+        pl.nchunk3 = (pl.nslot + pl.spb - 1) / pl.spb;
+        if (pl.nchunk3 < 1) pl.nchunk3 = 1;
+        pl.off_logits = 0;
+        pl.off_part1 = align256(bh * pl.nslot * sizeof(float));
         pl.off_part3 = pl.off_part1 + align256(bh * pl.nchunk1 * 3 * sizeof(float));
         pl.bytes = pl.off_part3 + align256(bh * pl.nchunk3 * d.D * sizeof(float));
-        // Entmax over many slots: the threshold candidates are compacted by
-        // many blocks (cand_kernel) instead of inside the one block per head.
-        const int ncc = (pl.nslot + kCandChunk - 1) / kCandChunk;
-        if (alpha > 1.0f && ncc >= 2 && ncc <= kCandMaxChunks) {
-            pl.ncc = ncc;
-            pl.off_cand = pl.bytes;
-            pl.off_ccnt = pl.off_cand + align256(bh * ncc * kCandPerChunk * sizeof(float));
-            pl.bytes = pl.off_ccnt + align256(bh * ncc * sizeof(int));
-        }
     }
     return pl;
 }

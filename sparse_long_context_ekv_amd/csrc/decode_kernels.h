@@ -1,31 +1,30 @@
-// Kernels of the sparse alpha-entmax decode over the selected pages ("EntmaxKV:
+// Kernels of the alpha-entmax decode over the selected pages ("EntmaxKV:
 // Support-Aware Decoding for Entmax Attention", section 4.1; alpha-entmax of
-// section 2.2; dropped mass of section 3.1).
+// section 2.2; dropped mass of section 3.1).  x = (alpha - 1) s, and only
+// x > max(x) - 1 can be in the support (the top term alone is at most 1).
+// Three paths:
 //
-//   logits_kernel  grid (page chunks, B*G): gathers each selected page-group
-//                  K tile (16 tokens x D, contiguous) through the page table,
-//                  one token per 16-lane row, and writes s = q.k/sqrt(D) for
-//                  the group's r heads into a [B][HQ][slots] workspace
-//                  (invalid slots -inf).  Per chunk and head it also keeps
-//                  (max, sum exp(s - max), valid count).
-//   tau_kernel     grid (HQ, B): the threshold of sum [x - tau]_+^beta = 1,
-//                  x = (alpha-1) s.  Only x > max(x) - 1 can be in the
-//                  support (the top term alone is at most 1), so those
-//                  candidates are compacted into LDS in slot order; Newton
-//                  steps from tau = max(x) - 1 (where the sum is >= 1) rise
-//                  monotonically to the root because the sum is convex and
-//                  decreasing in tau (beta >= 1); for beta = 1 and 2 the
-//                  closed form on the support found then gives tau exactly
-//                  (beta = 2: tau = m - sqrt((1 - V)/k), m the mean and V the
-//                  centred sum of squares of the k support values).  alpha = 1
-//                  (softmax) takes the log-partition straight from the chunk
-//                  partials.
-//   pv_kernel      grid (slot chunks, B*G): p = [x - tau]_+^beta has exact
-//                  zeros, so only slots with p > 0 for some head of the group
-//                  are compacted and only their V rows are read; partial sums
-//                  need no rescaling.
-//   reduce_kernel  grid (HQ, B): fixed-order sum of the chunk partials.
-// No atomics: every result is bitwise reproducible.
+//  fused (alpha > 1, at most kFusedMaxSlots selected slots per head):
+//   logits_kernel         grid (chunks of 8 selected pages, B*G): gathers each
+//                         page-group K tile (16 tokens x D, contiguous)
+//                         through the page table, one token per 16-lane row,
+//                         and writes s = q.k/sqrt(D) for the group's r heads
+//                         into a [B][HQ][slots] workspace (invalid slots -inf);
+//   sparse_tau_pv_kernel  one block per (b, g): candidates, threshold
+//                         (TauIter), support, PV over the support rows.
+//  streamed (alpha > 1 otherwise: full cache, long selections): no logits are
+//   kept; cand_stream_mfma_kernel (bf16 keys) or cand_stream_kernel ->
+//   stream_tau_kernel -> support_pv_kernel -> reduce_kernel (see "streamed
+//   entmax" below).
+//  softmax (alpha = 1): logits_kernel with per-chunk (max, sum exp(s - max),
+//   count) -> softmax_tau_kernel (log-partition) -> pv_kernel (every slot,
+//   p = exp(s - tau)) -> reduce_kernel (fixed-order sum of chunk partials).
+// Bitwise reproducible: the one atomic (the bf16 candidate stream's running
+// max, shared by a block's waves in LDS) only decides which extra entries
+// below the final filter its lists hold, and the threshold kernel orders the
+// candidates it keeps by list and slot.  (Past kCandCap candidates per head,
+// where the threshold kernel reads the lists directly, sums may round
+// differently from run to run.)
 //
 // This header is compiled once per KV element type (decode_bf16.hip,
 // decode_f32.hip), so that the two sets of instantiations build in parallel.
@@ -39,76 +38,43 @@ namespace ekv {
 enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
 constexpr int kLogitUnroll = 4;
 constexpr int kMaxLogitPpb = 32;       // pages per logits block at most (plan_decode: 8 or 32)
-constexpr int kCandCap = 8192;        // threshold candidates per head kept in LDS (general path)
-constexpr int kCandChunk = 4096;      // slots per cand_kernel block (256 threads x 16)
-constexpr int kCandPerChunk = 1024;   // candidates a chunk may hand over; more: the chunk overflows
-constexpr int kCandMaxChunks = 1024;  // chunks per head at most on the cand_kernel path
+constexpr int kCandCap = 8192;        // threshold candidates per head gathered in LDS (streamed path)
 
 // -------------------------------------------------------------- logits ----
-// PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
-// which the general threshold kernel reads (softmax, full cache).
-template <typename T, int D, int R, bool PART>
-__global__ __launch_bounds__(256) void logits_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int lg_ppb,
-    int nslot, int nchunk1, float inv_sqrt_d, float* __restrict__ logits, float* __restrict__ part1) {
+// Logits of a block's selected pages i0 .. i1-1, whose logical page and
+// physical tile were resolved into sh_lp / sh_phys (indexed from i0; -1 =
+// not readable): one token row per 16-lane row, the r heads' dot products
+// by fixed-order row sums, s = q.k/sqrt(D) stored at st[(i - i0) * kPage]
+// by lane j < R for head j (st already offset by the head and the row),
+// -inf for tokens past the sequence end or on unreadable pages.  PART also
+// keeps the row's running (max, sum exp(s - max), count) for head `lane`.
+// UNROLL pages' tiles per row are in flight at once.
+template <typename T, int D, int R, bool PART, int UNROLL = kLogitUnroll>
+__device__ __forceinline__ void chunk_logits(const Vec<T, D / kRow> (&qv)[R], const T* __restrict__ k_cache,
+                                             const int* sh_lp, const int* sh_phys, int i0, int i1, int ppb, int n,
+                                             int G, int g, int lane, int row, float inv_sqrt_d, float* st,
+                                             float& run_m, float& run_l, float& run_c) {
     constexpr int CH = D / kRow;
     constexpr int NW = Vec<T, CH>::NW;
-    extern __shared__ float stage[];           // [R][ppb * kPage] logits of this chunk
-    __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
-    __shared__ int sh_lp[kMaxLogitPpb], sh_phys[kMaxLogitPpb];
-    const int ppb = 1 << lg_ppb;
-    const int unit = blockIdx.y;
-    const int b = unit / G, g = unit - b * G;
-    const int HQ = G * R;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int i0 = blockIdx.x * ppb;
-    const int i1 = min(cnt, i0 + ppb);
-    const int lane = threadIdx.x & (kRow - 1);
-    const int row = threadIdx.x >> 4;          // token within the page
-
-    Vec<T, CH> qv[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
-
-    float* st = stage + ((lane < R ? lane : 0) << (lg_ppb + 4)) + row;   // lane j < R: head j
-    float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
-    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
-
-    // The chunk's pages: logical index and physical tile, resolved once (one
-    // selection -> page-table chain per block instead of one per page and row).
-    for (int t = threadIdx.x; t < ppb; t += blockDim.x) {
-        const int ii = i0 + t;
-        const int lp = ii < i1 ? (sel ? sel[ii] : ii) : -1;
-        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
-        const bool ok = phys >= 0 && phys < NP;
-        sh_lp[t] = ok ? lp : -1;
-        sh_phys[t] = ok ? phys : -1;
-    }
-    __syncthreads();
-
-    for (int i = i0; i < i1; i += kLogitUnroll) {
-        Vec<T, CH> kv[kLogitUnroll];
-        int lp[kLogitUnroll], phys[kLogitUnroll];
-        bool ok[kLogitUnroll];
+    for (int i = i0; i < i1; i += UNROLL) {
+        Vec<T, CH> kv[UNROLL];
+        int lp[UNROLL], phys[UNROLL];
+        bool ok[UNROLL];
         // Branch-free, so that all loads of the unroll are in flight at once
         // (a load under a per-page branch waits for the previous ones); an
         // empty slot reads page 0 and is ignored.
 #pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u) {
+        for (int u = 0; u < UNROLL; ++u) {
             const int t = min(i + u - i0, ppb - 1);
             lp[u] = i + u < i1 ? sh_lp[t] : -1;
             phys[u] = sh_phys[t];
             ok[u] = lp[u] >= 0;
         }
 #pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u)
+        for (int u = 0; u < UNROLL; ++u)
             kv[u].load(k_cache + (((size_t)(ok[u] ? phys[u] : 0) * G + g) * kPage + row) * D + lane * CH);
 #pragma unroll
-        for (int u = 0; u < kLogitUnroll; ++u) {
+        for (int u = 0; u < UNROLL; ++u) {
             const int ii = i + u;
             if (ii >= i1) break;                       // block-uniform
             float mine = -INFINITY;
@@ -145,6 +111,170 @@ __global__ __launch_bounds__(256) void logits_kernel(
             }
         }
     }
+}
+
+
+// The same logits on the matrix cores, for bf16 keys: a page's 16 tokens
+// against the group's r <= 8 queries is a small dense contraction,
+// logits[head][token] = sum_c q[head][c] k[token][c], done by D/32
+// v_mfma_f32_16x16x32_bf16 per page (rows = heads, padded to 16 with
+// zeros; columns = the page's tokens).  In the MFMA's operand layout lane
+// l (token or head t = l % 16, quarter h = l / 16) supplies the 8 channels
+// 32 i + 8 h .. 32 i + 8 h + 7 of instruction i, so one load instruction
+// of the wave reads 64 contiguous bytes of each of the page's 16 tokens,
+// and the result leaves heads 4h .. 4h + 3 of token t in lane l.  Each
+// wave takes every 4th page of the chunk, UNROLL pages in flight; results
+// go to stage[head * stride + (page - i0) * 16 + token] (-inf past the
+// sequence end or on an unreadable page).  Needs 256-thread blocks.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The query operand: lane l holds channels 32 i + 8 (l / 16) .. + 7 of head
+// l % 16 for instruction i (zeros for rows past the group's R heads).
+template <int D, int R>
+struct MfmaQ {
+    bf16x8_t a[D / 32];
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ qrow) {
+        static_assert(R <= 16 && D % 32 == 0, "one 16-row tile of heads, whole 32-channel slices");
+        const int l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+            const uint4 v = tq < R ? *reinterpret_cast<const uint4*>(qrow + (size_t)tq * D + 32 * t + 8 * hq)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+            a[t] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+};
+
+// UNROLL pages of one wave in registers: pages i, i + 4, ..., i + 4 (UNROLL
+// - 1) of the chunk [i0, i1).  load() issues every read without branches (a
+// page past the chunk or unreadable reads page 0 and is ignored); logits()
+// contracts them with the query tile and writes stage[head * stride +
+// (page - i0) * 16 + token].
+template <int D, int UNROLL>
+struct MfmaKPages {
+    bf16x8_t kb[UNROLL][D / 32];
+    bool ok[UNROLL];
+    int lp[UNROLL];
+
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ k_cache, const int* sh_lp, const int* sh_phys,
+                                         int i, int i0, int i1, int G, int g) {
+        const int l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int ii = i + 4 * u;
+            const int t = ii < i1 ? ii - i0 : 0;
+            const int ph = sh_phys[t];
+            lp[u] = sh_lp[t];
+            ok[u] = ii < i1 && ph >= 0;
+            const bf16_t* src = k_cache + (((size_t)(ok[u] ? ph : 0) * G + g) * kPage + tq) * D + 8 * hq;
+#pragma unroll
+            for (int t2 = 0; t2 < D / 32; ++t2)
+                kb[u][t2] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + 32 * t2));
+        }
+    }
+
+    // Every page's 16 x 16 product (pages past the chunk too: their reads
+    // were of page 0 and the caller ignores them), no branches.
+    template <int R>
+    __device__ __forceinline__ void contract(const MfmaQ<D, R>& q, f32x4_t (&acc)[UNROLL]) const {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t2 = 0; t2 < D / 32; ++t2)
+                acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[t2], kb[u][t2], acc[u], 0, 0, 0);
+        }
+    }
+
+    template <int R>
+    __device__ __forceinline__ void logits(const MfmaQ<D, R>& q, int i, int i0, int i1, int n, float inv_sqrt_d,
+                                           float* stage, int stride) const {
+        const int l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int ii = i + 4 * u;
+            if (ii < i1) {                                          // wave-uniform
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t2 = 0; t2 < D / 32; ++t2)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[t2], kb[u][t2], acc, 0, 0, 0);
+                const bool live = ok[u] && lp[u] * kPage + tq < n;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int head = 4 * hq + j;
+                    if (head < R)
+                        stage[head * stride + (ii - i0) * kPage + tq] = live ? acc[j] * inv_sqrt_d : -INFINITY;
+                }
+            }
+        }
+    }
+};
+
+template <int D, int R, int UNROLL>
+__device__ __forceinline__ void chunk_logits_mfma(const bf16_t* __restrict__ qrow, const bf16_t* __restrict__ k_cache,
+                                                  const int* sh_lp, const int* sh_phys, int i0, int i1, int n, int G,
+                                                  int g, float inv_sqrt_d, float* stage, int stride) {
+    MfmaQ<D, R> qa;
+    qa.load(qrow);
+    for (int i = i0 + (int)(threadIdx.x >> 6); i < i1; i += 4 * UNROLL) {     // wave-uniform
+        MfmaKPages<D, UNROLL> kp;
+        kp.load(k_cache, sh_lp, sh_phys, i, i0, i1, G, g);
+        kp.template logits<R>(qa, i, i0, i1, n, inv_sqrt_d, stage, stride);
+    }
+}
+
+// PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
+// which the general threshold kernel reads (softmax, full cache).
+template <typename T, int D, int R, bool PART>
+__global__ __launch_bounds__(256) void logits_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int lg_ppb,
+    int nslot, int nchunk1, float inv_sqrt_d, float* __restrict__ logits, float* __restrict__ part1) {
+    constexpr int CH = D / kRow;
+    extern __shared__ float stage[];           // [R][ppb * kPage] logits of this chunk
+    __shared__ float sh_m[kRow][R], sh_l[kRow][R], sh_c[kRow][R];
+    __shared__ int sh_lp[kMaxLogitPpb], sh_phys[kMaxLogitPpb];
+    const int ppb = 1 << lg_ppb;
+    const int unit = blockIdx.y;
+    const int b = unit / G, g = unit - b * G;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int i0 = blockIdx.x * ppb;
+    const int i1 = min(cnt, i0 + ppb);
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;          // token within the page
+
+    Vec<T, CH> qv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
+
+    float* st = stage + ((lane < R ? lane : 0) << (lg_ppb + 4)) + row;   // lane j < R: head j
+    float run_m = -INFINITY, run_l = 0.0f, run_c = 0.0f;
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+
+    // The chunk's pages: logical index and physical tile, resolved once (one
+    // selection -> page-table chain per block instead of one per page and row).
+    for (int t = threadIdx.x; t < ppb; t += blockDim.x) {
+        const int ii = i0 + t;
+        const int lp = ii < i1 ? (sel ? sel[ii] : ii) : -1;
+        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
+        const bool ok = phys >= 0 && phys < NP;
+        sh_lp[t] = ok ? lp : -1;
+        sh_phys[t] = ok ? phys : -1;
+    }
+    __syncthreads();
+
+    if constexpr (!PART && std::is_same<T, bf16_t>::value) {
+        chunk_logits_mfma<D, R, 2>(q + ((size_t)b * HQ + g * R) * D, k_cache, sh_lp, sh_phys, i0, i1, n, G, g,
+                                   inv_sqrt_d, stage, ppb * kPage);
+    } else {
+        chunk_logits<T, D, R, PART>(qv, k_cache, sh_lp, sh_phys, i0, i1, ppb, n, G, g, lane, row, inv_sqrt_d, st,
+                                    run_m, run_l, run_c);
+    }
     if (PART && lane < R) {
         sh_m[row][lane] = run_m;
         sh_l[row][lane] = run_l;
@@ -175,10 +305,6 @@ __global__ __launch_bounds__(256) void logits_kernel(
 }
 
 // ----------------------------------------------------------------- tau ----
-struct TauSums {
-    float s1, s0, k;
-};
-
 __device__ __forceinline__ float powb(float d, int mode, float beta) {
     return mode == kModeBeta1 ? d : (mode == kModeBeta2 ? d * d : powf(d, beta));
 }
@@ -279,29 +405,18 @@ __device__ __forceinline__ void tau_iter_step(TauIter& st, float lo, float beta,
     }
 }
 
-static __global__ __launch_bounds__(256) void tau_kernel(
-    const float* __restrict__ logits, const float* __restrict__ part1,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
-    int mode, float alpha, float beta, const float* __restrict__ tau_hint, const float* __restrict__ tau_ref,
+// Softmax (alpha = 1): the log-partition log sum_j exp(s_j) from the
+// logits kernel's chunk partials (max, sum exp(s - max), count), combined in
+// a fixed order; every valid token is in the support, and the kept mass
+// under tau_ref is sum_j exp(s_j - tau_ref).  grid (HQ, B).
+static __global__ __launch_bounds__(256) void softmax_tau_kernel(
+    const float* __restrict__ part1, int HQ, int nchunk1, const float* __restrict__ tau_ref,
     float* __restrict__ tau_out, int32_t* __restrict__ support_out, float* __restrict__ delta_out,
-    int32_t* __restrict__ supref_out, const float* __restrict__ ccand, const int32_t* __restrict__ ccnt, int ncc) {
-    __shared__ float cand[kCandCap];
-    __shared__ int coff[kCandMaxChunks + 1];
+    int32_t* __restrict__ supref_out) {
     __shared__ float red[8];
-    __shared__ int wsum[8];
-    __shared__ float red5[2][4][5];
-    int phase = 0, p5 = 0;
+    int phase = 0;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int R = HQ / G;
-    const int unit = b * G + h / R;
-    const int n = seq_len_at(seq_lens, b, MP);
-    const int M = num_pages(n);
-    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int nused = cnt * kPage;
     const size_t oh = (size_t)b * HQ + h;
-
-    // Combine the chunk partials (fixed order).
     const float* pm = part1 + oh * nchunk1 * 3;
     float mx = -INFINITY;
     for (int c = threadIdx.x; c < nchunk1; c += 256) mx = fmaxf(mx, pm[c * 3]);
@@ -314,7 +429,6 @@ static __global__ __launch_bounds__(256) void tau_kernel(
     }
     L = block_sum<4>(L, red, phase);
     C = block_sum<4>(C, red, phase);
-    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
     if (!(C > 0.0f)) {
         if (threadIdx.x == 0) {
             tau_out[oh] = -INFINITY;
@@ -324,114 +438,464 @@ static __global__ __launch_bounds__(256) void tau_kernel(
         }
         return;
     }
-    if (mode == kModeSoftmax) {
-        const float lse = mx + logf(L);
-        float kept = 0.0f;
-        if (delta_out) {
-            for (int c = threadIdx.x; c < nchunk1; c += 256) {
-                const float m = pm[c * 3];
-                if (m > -INFINITY) kept += pm[c * 3 + 1] * expf(m - tref);
-            }
-            kept = block_sum<4>(kept, red, phase);
+    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+    float kept = 0.0f;
+    if (delta_out) {
+        for (int c = threadIdx.x; c < nchunk1; c += 256) {
+            const float m = pm[c * 3];
+            if (m > -INFINITY) kept += pm[c * 3 + 1] * expf(m - tref);
         }
+        kept = block_sum<4>(kept, red, phase);
+    }
+    if (threadIdx.x == 0) {
+        tau_out[oh] = mx + logf(L);
+        if (support_out) support_out[oh] = (int32_t)C;
+        if (delta_out) delta_out[oh] = 1.0f - kept;
+        if (supref_out) supref_out[oh] = (int32_t)C;      // softmax: every token has p > 0
+    }
+}
+
+// --------------------------------------------- streamed entmax (general) ----
+// alpha > 1 over the full cache or over a selection past the fused kernel's
+// slots.  No logits are kept: only x > max(x) - 1 can be in the support (the
+// top term alone is at most 1), so
+//   cand_stream_kernel  grid (splits * B*G): a block walks a contiguous range
+//                       of up to kStreamMaxChunks chunks of kStreamPpb pages,
+//                       computes the r heads' logits of each chunk in LDS and
+//                       keeps, per head, the chunk's x > (running max) - 1,
+//                       the running max being the largest x of the block's
+//                       chunks so far: every x > (global max) - 1 is kept,
+//                       and the filter tightens as the block goes.  Output per
+//                       (b, h, split): the list (x, slot) in slot order, its
+//                       count and the block's max;
+//   cand_stream_mfma_kernel  the same for bf16 keys, on the matrix cores, one
+//                       list per wave (described at the kernel);
+//   stream_tau_kernel   grid (HQ, B): global max from the list maxima; the
+//                       lists read by flat index (all threads, independent
+//                       loads), candidates above (global max) - 1 gathered
+//                       into LDS (or read from the lists when they do not
+//                       fit); the threshold by TauIter, support size, dropped
+//                       mass, and the support list (p, slot);
+//   support_pv_kernel   grid (kSupSplit, HQ, B): V rows of the support only,
+//                       partial sums per split, summed by reduce_kernel.
+constexpr int kStreamPpb = 32;                        // pages per chunk
+constexpr int kStreamSlots = kStreamPpb * kPage;      // 512 slots per chunk
+constexpr int kStreamMaxChunks = 64;                  // chunks per candidate-stream block at most
+constexpr int kStreamMaxLists = 2048;                 // candidate lists per (b, h) at most (4 per block)
+constexpr int kStreamStage = 1024;                    // candidates staged in LDS per wave (bf16 stream)
+constexpr int kStreamBlocks = 512;                    // aim: about this many candidate-stream blocks (2 per CU)
+constexpr int kSupSplit = 8;                          // PV blocks per head over its support
+constexpr int kStreamUnroll = 8;                      // pages' tiles in flight per row while streaming
+
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void cand_stream_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int cpb, int nsplit,
+    float inv_sqrt_d, float a, float2* __restrict__ cands, int32_t* __restrict__ ccount, float* __restrict__ cmax) {
+    constexpr int CH = D / kRow;
+    constexpr int JPW = (R + 3) / 4;                     // heads per wave
+    constexpr int XPL = kStreamSlots / 64;
+    __shared__ float stage[R * kStreamSlots];            // [R][slots] logits of the current chunk
+    __shared__ int sh_lp[kStreamMaxChunks * kStreamPpb], sh_phys[kStreamMaxChunks * kStreamPpb];
+    // Block order: group fastest, then split, then sequence, so the G blocks
+    // that run side by side read the same logical pages of one sequence (the
+    // G tiles of a physical page are adjacent in the cache).
+    const int g = blockIdx.x % G, rest = blockIdx.x / G;
+    const int split = rest % nsplit, b = rest / nsplit;
+    const int unit = b * G + g;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int span = cpb * kStreamPpb;              // <= kStreamMaxChunks * kStreamPpb (the plan's cap)
+    const int p0 = split * span;
+    const int p1 = span <= kStreamMaxChunks * kStreamPpb ? min(cnt, p0 + span) : p0;   // else: an empty range
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    const int wv = threadIdx.x >> 6, l64 = threadIdx.x & 63;
+    const size_t lcap = (size_t)span * kPage;             // list capacity: every slot of the range
+
+    Vec<T, CH> qv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qv[j].load(q + ((size_t)b * HQ + g * R + j) * D + lane * CH);
+    // Every page of the range resolved at once (selection -> page table).
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+    for (int t = threadIdx.x; t < min(span, kStreamMaxChunks * kStreamPpb); t += blockDim.x) {
+        const int ii = p0 + t;
+        const int lp = ii < p1 ? (sel ? sel[ii] : ii) : -1;
+        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
+        const bool ok = phys >= 0 && phys < NP;
+        sh_lp[t] = ok ? lp : -1;
+        sh_phys[t] = ok ? phys : -1;
+    }
+    __syncthreads();
+
+    float rmax[JPW];
+    int rcnt[JPW];
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj) {
+        rmax[jj] = -INFINITY;
+        rcnt[jj] = 0;
+    }
+    float* st = stage + (lane < R ? lane : 0) * kStreamSlots + row;
+    for (int c = 0; c < cpb; ++c) {
+        const int i0 = p0 + c * kStreamPpb;
+        if (i0 >= p1) break;                                 // block-uniform
+        const int i1 = min(p1, i0 + kStreamPpb);
+        float rm = -INFINITY, rl = 0.0f, rc = 0.0f;
+        chunk_logits<T, D, R, false, kStreamUnroll>(qv, k_cache, sh_lp + c * kStreamPpb, sh_phys + c * kStreamPpb,
+                                                    i0, i1, kStreamPpb, n, G, g, lane, row, inv_sqrt_d, st, rm, rl,
+                                                    rc);
+        __syncthreads();
+        const int nsl = (i1 - i0) * kPage;
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            const int j = wv + 4 * jj;
+            if (j >= R) break;                               // wave-uniform
+            const float* sj = stage + j * kStreamSlots;
+            float xs[XPL];
+            float m = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < XPL; ++k) {
+                const int idx = k * 64 + l64;
+                xs[k] = idx < nsl ? a * sj[idx] : -INFINITY;
+                m = fmaxf(m, xs[k]);
+            }
+            rmax[jj] = fmaxf(rmax[jj], wave_max(m));
+            const float lo = rmax[jj] - 1.0f;               // -inf: nothing valid yet
+            float2* dst = cands + (((size_t)b * HQ + g * R + j) * nsplit + split) * lcap;
+#pragma unroll
+            for (int k = 0; k < XPL; ++k) {
+                const bool f = xs[k] > lo;
+                const uint64_t bal = __ballot(f);
+                if (f) dst[rcnt[jj] + lanes_below(bal)] = make_float2(xs[k], __int_as_float(i0 * kPage + k * 64 + l64));
+                rcnt[jj] += __popcll(bal);
+            }
+        }
+        __syncthreads();                                     // the stage is rewritten by the next chunk
+    }
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj) {
+        const int j = wv + 4 * jj;
+        if (j < R && l64 == 0) {
+            const size_t rcx = ((size_t)b * HQ + g * R + j) * nsplit + split;
+            ccount[rcx] = rcnt[jj];
+            cmax[rcx] = rmax[jj];
+        }
+    }
+}
+
+// bf16 keys: the same filter with every wave on its own pages (pages
+// p0 + w, p0 + w + 4, ... of the block's range, in steps of 8 pages, on the
+// matrix cores) and its own list per head, so that after the page table is
+// resolved no barrier couples the block's waves: each keeps its next
+// step's reads in flight while it takes this step's candidates.  The
+// candidates are staged in LDS (kStreamStage entries per wave, split over
+// the r heads) and copied out only when this step could overflow a buffer
+// (before the next step's reads are issued, so that the wait for those
+// reads does not also wait for fresh stores) and at the end.  The running
+// max is shared by the block's waves through an LDS atomic max (any value
+// read is a logit of the block, so still every x > (global max) - 1 is
+// kept).  Lists per (b, h, split, wave) of capacity cpb * 128 slots, in
+// slot order.
+template <int D, int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cand_stream_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
+    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int cpb, int nsplit,
+    float inv_sqrt_d, float a, float2* __restrict__ cands, int32_t* __restrict__ ccount, float* __restrict__ cmax) {
+    constexpr int KPW = R <= 4 ? 8 : 4;                  // pages per wave per step (32 or 16 KiB in flight)
+    constexpr int SP = 4 * KPW;                          // pages per block step
+    constexpr int CB = kStreamStage / R;                 // staged candidates per (wave, head)
+    constexpr int NR = (R + 3) / 4;                      // rows of lanes that hold heads
+    static_assert(CB >= 2 * KPW * kPage, "a step adds at most KPW * 16 candidates per head");
+    static_assert(kStreamPpb % (4 * KPW) == 0, "whole steps per chunk");
+    __shared__ float2 stage[4][kStreamStage];
+    __shared__ uint32_t smax[R];                         // the block's running max per head (ord_key)
+    __shared__ int sh_lp[kStreamMaxChunks * kStreamPpb], sh_phys[kStreamMaxChunks * kStreamPpb];
+    // Block order: group fastest, then split, then sequence (see cand_stream_kernel).
+    const int g = blockIdx.x % G, rest = blockIdx.x / G;
+    const int split = rest % nsplit, b = rest / nsplit;
+    const int unit = b * G + g;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int span = cpb * kStreamPpb;              // <= kStreamMaxChunks * kStreamPpb (the plan's cap)
+    const int p0 = split * span;
+    const int p1 = span <= kStreamMaxChunks * kStreamPpb ? min(cnt, p0 + span) : p0;   // else: an empty range
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+    for (int t = threadIdx.x; t < min(span, kStreamMaxChunks * kStreamPpb); t += blockDim.x) {
+        const int ii = p0 + t;
+        const int lp = ii < p1 ? (sel ? sel[ii] : ii) : -1;
+        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
+        const bool ok = phys >= 0 && phys < NP;
+        sh_lp[t] = ok ? lp : -1;
+        sh_phys[t] = ok ? phys : -1;
+    }
+    if (threadIdx.x < R) smax[threadIdx.x] = ord_key(-INFINITY);
+    __syncthreads();
+
+    // Lane l: token tq = l % 16 of a page, heads 4 hq .. 4 hq + 3 (hq = l / 16).
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+    const size_t lcap = (size_t)cpb * (kStreamPpb / 4) * kPage;   // a quarter of the range's slots
+    const uint32_t below = (1u << tq) - 1u;
+    float rmax[4];
+    int rcnt[4], scnt[4];                                  // copied out / staged (the row's head)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        rmax[j] = -INFINITY;
+        rcnt[j] = 0;
+        scnt[j] = 0;
+    }
+    // the row's staging buffers: head 4 hq + j at buf + j * CB
+    float2* const buf = &stage[wv][min(4 * hq, R - 1) * CB];
+    // A full stage (or the end): by the whole wave, head by head (only this
+    // wave touches its stage; head h's counts live in row h / 4, register
+    // h % 4), first drop the staged x <= (block max so far) - 1, compacting
+    // in place; then, at the end or if the stage is still too full, copy it
+    // out to the wave's list.
+    auto flush = [&](bool last) {
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+            const int jr = h & 3, rl = 16 * (h >> 2);
+            const int c = __builtin_amdgcn_readlane(scnt[jr], rl);
+            const float m = fmaxf(readlane(rmax[jr], rl),
+                                  ord_unkey(__hip_atomic_load(&smax[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+            const float lo = m - 1.0f;
+            float2* const src = &stage[wv][h * CB];
+            int keep = 0;
+            for (int e0 = 0; e0 < c; e0 += 4 * 64) {        // wave-uniform
+                float2 v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e = e0 + k * 64 + l;
+                    v[k] = src[e < c ? e : 0];
+                }
+                // every read of the batch is issued before its first write,
+                // and a kept entry only moves down
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bool kf = e0 + k * 64 + l < c && v[k].x > lo;
+                    const uint64_t bal = __ballot(kf);
+                    if (kf) src[keep + lanes_below(bal)] = v[k];
+                    keep += __popcll(bal);
+                }
+            }
+            int r0 = __builtin_amdgcn_readlane(rcnt[jr], rl);
+            if (last || keep > CB - KPW * kPage) {               // wave-uniform
+                float2* dst = cands + ((((size_t)b * HQ + g * R + h) * nsplit + split) * 4 + wv) * lcap + r0;
+                for (int e0 = 0; e0 < keep; e0 += 4 * 64) {
+                    float2 v[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = e0 + k * 64 + l;
+                        v[k] = src[e < keep ? e : 0];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (e0 + k * 64 + l < keep) dst[e0 + k * 64 + l] = v[k];
+                }
+                r0 += keep;
+                keep = 0;
+            }
+            if ((l >> 4) == (h >> 2)) {
+                scnt[jr] = keep;
+                rcnt[jr] = r0;
+                rmax[jr] = fmaxf(rmax[jr], m);
+            }
+        }
+    };
+    MfmaQ<D, R> mq;
+    mq.load(q + ((size_t)b * HQ + g * R) * D);
+    MfmaKPages<D, KPW> kp;
+    if (p0 < p1) kp.load(k_cache, sh_lp, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g);
+    for (int i0 = p0; i0 < p1; i0 += SP) {                  // block-uniform
+        const int i1 = min(p1, i0 + SP);
+        f32x4_t acc[KPW];
+        kp.template contract<R>(mq, acc);
+        bool full = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) full |= scnt[j] > CB - KPW * kPage;
+        if (__ballot(full)) flush(false);                    // wave-uniform
+        bool live[KPW];
+#pragma unroll
+        for (int u = 0; u < KPW; ++u) live[u] = i0 + wv + 4 * u < i1 && kp.ok[u] && kp.lp[u] * kPage + tq < n;
+        float x[KPW][4];
+        float lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < KPW; ++u) {
+                x[u][j] = live[u] ? a * (acc[u][j] * inv_sqrt_d) : -INFINITY;
+                m = fmaxf(m, x[u][j]);
+            }
+            rmax[j] = fmaxf(rmax[j], row_max16(m));          // the row's head 4 hq + j
+            if (4 * hq + j < R) rmax[j] = fmaxf(rmax[j], ord_unkey(atomicMax(&smax[4 * hq + j], ord_key(rmax[j]))));
+            lo[j] = rmax[j] - 1.0f;                          // -inf: nothing valid yet
+        }
+        // the next step's reads go out before this step's candidates are taken
+        if (i1 < p1) kp.load(k_cache, sh_lp + (i1 - p0), sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
+#pragma unroll
+        for (int u = 0; u < KPW; ++u) {
+            const float slot = __int_as_float((i0 + wv + 4 * u) * kPage + tq);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool f = 4 * hq + j < R && x[u][j] > lo[j];
+                // this row's lanes (one row of heads: row 0, the same for every lane)
+                const uint32_t rb = (uint32_t)(__ballot(f) >> (NR == 1 ? 0 : 16 * hq)) & 0xffffu;
+                if (f) buf[j * CB + scnt[j] + __popc(rb & below)] = make_float2(x[u][j], slot);
+                scnt[j] += __popc(rb);
+            }
+        }
+    }
+    flush(true);
+    if (tq == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int head = 4 * hq + j;
+            if (head < R) {
+                const size_t rcx = (((size_t)b * HQ + g * R + head) * nsplit + split) * 4 + wv;
+                ccount[rcx] = rcnt[j];
+                cmax[rcx] = rmax[j];
+            }
+        }
+    }
+}
+
+static __global__ __launch_bounds__(256) void stream_tau_kernel(
+    const float2* __restrict__ cands, const int32_t* __restrict__ ccount, const float* __restrict__ cmax,
+    int nsplit, int lcap, int HQ, int nslot, int mode, float beta, const float* __restrict__ tau_hint,
+    const float* __restrict__ tau_ref, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
+    float* __restrict__ delta_out, int32_t* __restrict__ supref_out, float2* __restrict__ sup_list,
+    int32_t* __restrict__ sup_count) {
+    constexpr int UNR = 8;                                // flat entries in flight per thread
+    __shared__ float cand[kCandCap];
+    __shared__ float cslot[kCandCap];                     // slot bits of each candidate
+    __shared__ int loff[kStreamMaxLists + 1];             // flat offset of each list
+    __shared__ float red[8];
+    __shared__ int wsum[8];
+    __shared__ float red5[2][4][5];
+    int phase = 0, p5 = 0;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const size_t oh = (size_t)b * HQ + h;
+    const float2* lists = cands + oh * nsplit * (size_t)lcap;
+    const int32_t* counts = ccount + oh * nsplit;
+
+    float xmax = -INFINITY;
+    for (int c = threadIdx.x; c < nsplit; c += 256) xmax = fmaxf(xmax, cmax[oh * nsplit + c]);
+    xmax = block_max<4>(xmax, red, phase);
+    if (!(xmax > -INFINITY)) {                             // no valid token
         if (threadIdx.x == 0) {
-            tau_out[oh] = lse;
-            if (support_out) support_out[oh] = (int32_t)C;
-            if (delta_out) delta_out[oh] = 1.0f - kept;
-            if (supref_out) supref_out[oh] = (int32_t)C;      // softmax: every token has p > 0
+            tau_out[oh] = -INFINITY;
+            if (support_out) support_out[oh] = 0;
+            if (delta_out) delta_out[oh] = 1.0f;
+            if (supref_out) supref_out[oh] = 0;
+            sup_count[oh] = 0;
         }
         return;
     }
+    const float lo = xmax - 1.0f;
 
-    const float a = alpha - 1.0f;
-    const float lo = a * mx - 1.0f;
-    const float* lrow = logits + oh * nslot;
-
-    // Candidates x > max(x) - 1, compacted in slot order: gathered from
-    // cand_kernel's per-chunk lists when it ran and no chunk overflowed (the
-    // same values in the same order), else by this block.
-    int ncand = 0;
-    bool gathered = false;
-    if (ccand) {
-        const int32_t* cc = ccnt + oh * ncc;
-        int mine[4], sum = 0;
-        bool over = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 4 * (int)threadIdx.x + i;
-            mine[i] = c < ncc ? cc[c] : 0;
-            over = over || mine[i] < 0;
-            sum += mine[i] > 0 ? mine[i] : 0;
+    // Flat offsets of the lists: thread t scans splits [t*per, (t+1)*per).
+    {
+        const int per = (nsplit + 255) / 256;
+        int local = 0;
+        for (int i = 0; i < per; ++i) {
+            const int c = threadIdx.x * per + i;
+            local += c < nsplit ? counts[c] : 0;
         }
         int ex, ex2, tot, tot2;
-        block_excl_scan2<4>(sum, over ? 1 : 0, ex, ex2, &tot, &tot2, wsum);
-        if (tot2 == 0 && tot <= kCandCap) {
-            int off = ex;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * (int)threadIdx.x + i;
-                if (c < ncc) coff[c] = off;
-                off += mine[i];
+        block_excl_scan2<4>(local, 0, ex, ex2, &tot, &tot2, wsum);
+        for (int i = 0; i < per; ++i) {
+            const int c = threadIdx.x * per + i;
+            if (c < nsplit) {
+                loff[c] = ex;
+                ex += counts[c];
             }
-            if (threadIdx.x == 0) coff[ncc] = tot;
-            __syncthreads();
-            const float* src = ccand + oh * (size_t)ncc * kCandPerChunk;
-            for (int e = threadIdx.x; e < tot; e += 256) {
-                int lo_c = 0, hi_c = ncc - 1;            // last chunk with coff[c] <= e
-                while (lo_c < hi_c) {
-                    const int mid = (lo_c + hi_c + 1) >> 1;
-                    if (coff[mid] <= e) lo_c = mid; else hi_c = mid - 1;
-                }
-                cand[e] = src[(size_t)lo_c * kCandPerChunk + (e - coff[lo_c])];
-            }
-            __syncthreads();
-            ncand = tot;
-            gathered = true;
         }
-    }
-    for (int base = 0; !gathered && base < nused; base += 256) {
-        const int sl = base + threadIdx.x;
-        const float x = sl < nused ? a * lrow[sl] : -INFINITY;
-        const bool f = x > lo;
-        const uint64_t m = __ballot(f);
-        const int wid = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) == 0) wsum[wid] = __popcll(m);
-        __syncthreads();
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            off += i < wid ? wsum[i] : 0;
-            tot += wsum[i];
-        }
-        const int pos = ncand + off + lanes_below(m);
-        if (f && pos < kCandCap) cand[pos] = x;
-        ncand += tot;
+        if (threadIdx.x == 0) loff[nsplit] = tot;
         __syncthreads();
     }
-    const bool in_lds = ncand <= kCandCap;
-
-    // Sums over the candidates (LDS), or over every slot with the same filter.
-    auto sums = [&](float t, float t_keep_above, bool want_s0) -> TauSums {
-        float s1 = 0.0f, s0 = 0.0f, k = 0.0f;
-        const int lim = in_lds ? ncand : nused;
-        for (int i = threadIdx.x; i < lim; i += 256) {
-            const float x = in_lds ? cand[i] : a * lrow[i];
-            const float dd = x - t;
-            if (x > t_keep_above && dd > 0.0f) {
-                s1 += powb(dd, mode, beta);
-                if (want_s0) s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? dd : powf(dd, beta - 1.0f));
-                k += 1.0f;
+    const int T = loff[nsplit];
+    // Every list entry, by flat index f = tid, tid + 256, ... (UNR loads in
+    // flight), in a fixed order: fn(x, slot bits).
+    auto each_flat = [&](auto&& fn) {
+        int sidx = 0;                                      // list of the current f, moved forward
+        for (int f0 = threadIdx.x; f0 < T; f0 += 256 * UNR) {
+            float2 e[UNR];
+            bool ok[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int f = f0 + u * 256;
+                ok[u] = f < T;
+                const int ff = ok[u] ? f : T - 1;        // past the end: the last entry (ignored); keeps sidx monotone
+                while (loff[sidx + 1] <= ff) ++sidx;
+                e[u] = lists[(size_t)sidx * lcap + (ff - loff[sidx])];
             }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (ok[u]) fn(e[u]);
         }
-        TauSums r;
-        r.s1 = block_sum<4>(s1, red, phase);
-        r.s0 = want_s0 ? block_sum<4>(s0, red, phase) : 0.0f;
-        r.k = block_sum<4>(k, red, phase);
-        return r;
     };
+    // Candidates x > lo into LDS in one pass over the lists: rounds of
+    // 256 * GUNR entries (all in flight at once; entry f0 + 256 u + t read by
+    // thread t), each candidate placed at its rank in flat order: the
+    // candidates of earlier rounds, of the round's earlier u, of earlier
+    // waves at this u, and of lower lanes (wave ballot).  So they land in
+    // list order and, within a list, in slot order, whatever else the lists
+    // hold: the set x > lo and that order fix every sum below.  If they do
+    // not all fit, the later passes read the lists instead.
+    constexpr int GUNR = 16;                              // GUNR * 4 (u, wave) pairs: one per lane of a wave
+    __shared__ int gbase[GUNR * 4 + 1];                   // per (u, wave): rank of its first candidate; round total
+    int total = 0;
+    {
+        const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+        int sidx = 0;
+        for (int f0 = 0; f0 < T; f0 += 256 * GUNR) {      // block-uniform
+            float2 e[GUNR];
+            uint64_t bal[GUNR];
+#pragma unroll
+            for (int u = 0; u < GUNR; ++u) {
+                const int f = f0 + u * 256 + (int)threadIdx.x;
+                const int ff = f < T ? f : T - 1;          // past the end: the last entry (ignored); keeps sidx monotone
+                while (loff[sidx + 1] <= ff) ++sidx;
+                e[u] = lists[(size_t)sidx * lcap + (ff - loff[sidx])];
+            }
+#pragma unroll
+            for (int u = 0; u < GUNR; ++u) {
+                bal[u] = __ballot(f0 + u * 256 + (int)threadIdx.x < T && e[u].x > lo);
+                if (ln == 0) gbase[u * 4 + wv] = __popcll(bal[u]);
+            }
+            __syncthreads();
+            if (wv == 0) {                                 // exclusive scan in (u, wave) order
+                const int c = gbase[ln];
+                const int inc = wave_incl_scan(c);
+                gbase[ln] = inc - c;
+                if (ln == 63) gbase[GUNR * 4] = inc;
+            }
+            __syncthreads();
+            const int tot = gbase[GUNR * 4];
+            if (total + tot <= kCandCap) {                 // block-uniform
+#pragma unroll
+                for (int u = 0; u < GUNR; ++u) {
+                    if ((bal[u] >> ln) & 1u) {
+                        const int pos = total + gbase[u * 4 + wv] + lanes_below(bal[u]);
+                        cand[pos] = e[u].x;
+                        cslot[pos] = e[u].y;
+                    }
+                }
+            }
+            total += tot;
+            __syncthreads();                               // gbase is rewritten by the next round
+        }
+    }
+    const bool in_lds = total <= kCandCap;
+    __syncthreads();
 
-    // Three block sums (fixed order), a minimum and a maximum with one
-    // barrier (red5 alternates, as block_sum's buffer does).
+    // Three block sums (fixed order), a minimum and a maximum, one barrier.
     auto block5 = [&](float v0, float v1, float v2, float vmin, float vmax, float* r) {
         const float a0 = wave_sum(v0), a1 = wave_sum(v1), a2 = wave_sum(v2);
         const float a3 = -wave_max(-vmin), a4 = wave_max(vmax);
@@ -457,30 +921,34 @@ static __global__ __launch_bounds__(256) void tau_kernel(
         }
         p5 ^= 1;
     };
+    // Every candidate x > lo, from LDS or from the lists.
+    auto each_cand = [&](auto&& fn) {
+        if (in_lds) {
+            for (int i = threadIdx.x; i < total; i += 256) fn(cand[i]);
+        } else {
+            each_flat([&](float2 e) {
+                if (e.x > lo) fn(e.x);
+            });
+        }
+    };
 
     float tau = lo;
     if (beta >= 1.0f) {
-        // From max - 1, or from tau_hint when it lies in (max - 1, max); each
-        // step one pass and one barrier (see TauIter).  The state is
-        // block-uniform: every thread steps on the same block sums.
-        TauIter st = tau_iter_start(lo, a * mx, tau_hint ? tau_hint[oh] : NAN, false);
-        const int lim = in_lds ? ncand : nused;
-        for (int it = 0; it < 100 && !st.done; ++it) {
+        TauIter st = tau_iter_start(lo, xmax, tau_hint ? tau_hint[oh] : NAN, false);
+        for (int it = 0; it < 100 && !st.done; ++it) {   // block-uniform state
             const float t = st.t;
             float s1 = 0.0f, s0 = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
-            for (int i = threadIdx.x; i < lim; i += 256) {
-                const float x = in_lds ? cand[i] : a * lrow[i];
-                if (!(x > lo)) continue;
-                const float dd = x - t;
-                if (dd > 0.0f) {
-                    s1 += powb(dd, mode, beta);
-                    s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? dd : powf(dd, beta - 1.0f));
+            each_cand([&](float x) {
+                const float d = x - t;
+                if (d > 0.0f) {
+                    s1 += powb(d, mode, beta);
+                    s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? d : powf(d, beta - 1.0f));
                     kk += 1.0f;
                     mn = fminf(mn, x);
                 } else {
                     rest = fmaxf(rest, x);
                 }
-            }
+            });
             float r[5];
             block5(s1, s0, kk, mn, rest, r);
             if (mode == kModeBeta1) tau_iter_step<kModeBeta1>(st, lo, beta, r[0], r[1], r[2], r[3], r[4]);
@@ -489,97 +957,136 @@ static __global__ __launch_bounds__(256) void tau_kernel(
         }
         tau = st.done ? st.tau : st.t;
     } else {
-        // beta < 1 (alpha > 2): the sum is not convex; bisect.
-        float hi = a * mx - powf(C, 1.0f - alpha);
-        float l2 = lo;
+        // beta < 1 (alpha > 2): bisection on [max - 1, max], where
+        // F(max - 1) >= 1 > 0 = F(max)
+        float l2 = lo, hi = xmax;
         for (int it = 0; it < 60; ++it) {
             const float mid = 0.5f * (l2 + hi);
-            const TauSums r = sums(mid, lo, false);
-            if (r.s1 - 1.0f >= 0.0f) l2 = mid; else hi = mid;
+            float s1 = 0.0f;
+            each_cand([&](float x) {
+                const float d = x - mid;
+                if (d > 0.0f) s1 += powf(d, beta);
+            });
+            float r[5];
+            block5(s1, 0.0f, 0.0f, 0.0f, 0.0f, r);
+            if (r[0] >= 1.0f) l2 = mid; else hi = mid;
         }
         tau = 0.5f * (l2 + hi);
     }
 
-    // Support size and dropped mass with respect to tau_ref.
-    const TauSums fin = sums(tau, lo, false);
-    TauSums ref = {0.0f, 0.0f, 0.0f};
-    if (delta_out || supref_out) ref = sums(tref, lo, false);     // tref >= tau >= lo
+    // Support size, dropped mass w.r.t. tau_ref (>= tau >= lo, so only
+    // candidates count), and the support list (p, slot) at per-thread offsets;
+    // from LDS, or from the lists when the candidates did not fit.
+    auto each_cand2 = [&](auto&& fn) {
+        if (in_lds) {
+            for (int i = threadIdx.x; i < total; i += 256) fn(make_float2(cand[i], cslot[i]));
+        } else {
+            each_flat([&](float2 e) {
+                if (e.x > lo) fn(e);
+            });
+        }
+    };
+    const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+    const bool want_ref = delta_out || supref_out;
+    int ns = 0;
+    float kept = 0.0f, nref = 0.0f;
+    each_cand2([&](float2 e) {
+        if (e.x > tau) ++ns;
+        if (want_ref && e.x > tref) {
+            kept += powb(e.x - tref, mode, beta);
+            nref += 1.0f;
+        }
+    });
+    int soff, soff2, stotal, st2;
+    block_excl_scan2<4>(ns, 0, soff, soff2, &stotal, &st2, wsum);
+    float2* sl_out = sup_list + oh * (size_t)nslot;
+    each_cand2([&](float2 e) {
+        if (e.x > tau) sl_out[soff++] = make_float2(powb(e.x - tau, mode, beta), e.y);
+    });
+    if (want_ref) {
+        kept = block_sum<4>(kept, red, phase);
+        nref = block_sum<4>(nref, red, phase);
+    }
     if (threadIdx.x == 0) {
         tau_out[oh] = tau;
-        if (support_out) support_out[oh] = (int32_t)fin.k;
-        if (delta_out) delta_out[oh] = 1.0f - ref.s1;
-        if (supref_out) supref_out[oh] = (int32_t)ref.k;
+        if (support_out) support_out[oh] = stotal;
+        if (delta_out) delta_out[oh] = 1.0f - kept;
+        if (supref_out) supref_out[oh] = (int32_t)nref;
+        sup_count[oh] = stotal;
     }
 }
 
-
-// Threshold candidates of the general entmax path, compacted by many blocks:
-// grid (ncc, HQ, B), block c of head (b, h) takes slots
-// [c*kCandChunk, (c+1)*kCandChunk) and writes its x = (alpha-1) s > max(x) - 1
-// in slot order to its own list of kCandPerChunk entries, with the count
-// (-1 when the list would overflow).  max(x) comes from the logits kernel's
-// chunk partials, combined as tau_kernel combines them, so tau_kernel can
-// gather the lists in chunk order into exactly the array it would build.
-static __global__ __launch_bounds__(256) void cand_kernel(
-    const float* __restrict__ logits, const float* __restrict__ part1,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int HQ, int MP, int nslot, int nchunk1,
-    float alpha, int ncc, float* __restrict__ ccand, int32_t* __restrict__ ccnt) {
-    __shared__ float red[8];
-    __shared__ int wsum[8];
-    int phase = 0;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int R = HQ / G;
-    const int unit = b * G + h / R;
+// V rows of the support list of head (b, h), split over kSupSplit blocks
+// (entries [count*split/kSupSplit, count*(split+1)/kSupSplit)): each 16-lane
+// row takes every 16th entry, PVU entries in flight (entry -> page of the
+// selection -> physical tile -> V row), then the rows and the block's waves
+// are summed in a fixed order into part3[(b, h)][split][D].
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void support_pv_kernel(
+    const T* __restrict__ v_cache, const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel_pages, const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP,
+    int NP, int nslot, const float2* __restrict__ sup_list, const int32_t* __restrict__ sup_count,
+    float* __restrict__ part3) {
+    constexpr int CH = D / kRow;
+    constexpr int PVU = 4;
+    __shared__ float wred[4][D];
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int HQ = gridDim.y;
+    const int g = h / R;
+    const int unit = b * G + g;
+    const size_t oh = (size_t)b * HQ + h;
     const int n = seq_len_at(seq_lens, b, MP);
     const int M = num_pages(n);
     const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
-    const int nused = cnt * kPage;
-    const size_t oh = (size_t)b * HQ + h;
-    int32_t* count = ccnt + oh * ncc + c;
-    const int s0 = c * kCandChunk;
-    if (s0 >= nused) {                       // block-uniform
-        if (threadIdx.x == 0) *count = 0;
-        return;
-    }
-    const float* pm = part1 + oh * nchunk1 * 3;
-    float mx = -INFINITY;
-    for (int i = threadIdx.x; i < nchunk1; i += 256) mx = fmaxf(mx, pm[i * 3]);
-    mx = block_max<4>(mx, red, phase);
-    const float a = alpha - 1.0f;
-    const float lo = a * mx - 1.0f;
-    // 16 consecutive slots per thread; nused is a multiple of 16 (whole
-    // pages), so a thread's slots are all used or all unused.
-    const int sb = s0 + 16 * (int)threadIdx.x;
-    float x[16];
-    if (sb < nused) {
-        const float4* p4 = reinterpret_cast<const float4*>(logits + oh * nslot + sb);
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+    const int32_t* pt = page_table + (size_t)b * MP;
+    const long total = sup_count[oh];
+    const int k0 = (int)(total * split / kSupSplit), k1 = (int)(total * (split + 1) / kSupSplit);
+    const float2* list = sup_list + oh * (size_t)nslot;
+    const int lane = threadIdx.x & (kRow - 1);
+    const int row = threadIdx.x >> 4;
+    float acc[CH];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 v = p4[i];
-            x[4 * i] = a * v.x;
-            x[4 * i + 1] = a * v.y;
-            x[4 * i + 2] = a * v.z;
-            x[4 * i + 3] = a * v.w;
+    for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+    for (int e0 = k0 + row; e0 < k1; e0 += PVU * kRow) {
+        Vec<T, CH> vv[PVU];
+        float pp[PVU];
+        bool ok[PVU];
+        // branch-free, so that the PVU chains are in flight together; an
+        // entry past the range re-reads entry e0 and is ignored
+#pragma unroll
+        for (int u = 0; u < PVU; ++u) {
+            const int e = e0 + u * kRow;
+            const float2 en = list[e < k1 ? e : e0];
+            const int slot = __float_as_int(en.y);
+            const int ip = slot >> 4;
+            const int lp = (ip >= 0 && ip < cnt) ? (sel ? sel[ip] : ip) : -1;
+            const int phys = (lp >= 0 && lp < M) ? pt[lp] : -1;
+            ok[u] = e < k1 && phys >= 0 && phys < NP;
+            pp[u] = ok[u] ? en.x : 0.0f;
+            vv[u].load(v_cache + (((size_t)(ok[u] ? phys : 0) * G + g) * kPage + (slot & (kPage - 1))) * D + lane * CH);
         }
-    } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = -INFINITY;
+        for (int u = 0; u < PVU; ++u)
+            if (ok[u])
+#pragma unroll
+                for (int c = 0; c < CH; ++c) acc[c] = fmaf(pp[u], vv[u].get(c), acc[c]);
     }
-    int k = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) k += x[i] > lo ? 1 : 0;
-    int ex, ex2, tot, tot2;
-    block_excl_scan2<4>(k, 0, ex, ex2, &tot, &tot2, wsum);
-    if (!(mx > -INFINITY) || tot > kCandPerChunk) {
-        if (threadIdx.x == 0) *count = mx > -INFINITY ? -1 : 0;
-        return;
+    for (int c = 0; c < CH; ++c) {
+        float v = acc[c];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[c] = v;
     }
-    float* dst = ccand + (oh * ncc + c) * kCandPerChunk;
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) < kRow) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        if (x[i] > lo) dst[ex++] = x[i];
-    if (threadIdx.x == 0) *count = tot;
+        for (int c = 0; c < CH; ++c) wred[wid][lane * CH + c] = acc[c];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256)
+        part3[(oh * kSupSplit + split) * D + c] = ((wred[0][c] + wred[1][c]) + wred[2][c]) + wred[3][c];
 }
 
 // ------------------------------------------------------------------ PV ----
@@ -1280,26 +1787,48 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
                                                         sel_stride, alpha, beta, logits, io, s);
         }
     }
+    if (pl.stream) {
+        float2* cands = (float2*)(ws + pl.off_cands);
+        int32_t* ccount = (int32_t*)(ws + pl.off_ccount);
+        float* cmax = (float*)(ws + pl.off_cmax);
+        float2* sup = (float2*)(ws + pl.off_sup);
+        int32_t* supcnt = (int32_t*)(ws + pl.off_supcnt);
+        // lists per split: one per wave on bf16 keys, one per block otherwise
+        int lps = 1;
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            lps = 4;
+            cand_stream_mfma_kernel<D, R><<<dim3(pl.nsplit_s * units), dim3(256), 0, s>>>(
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP, pl.cpb_s,
+                pl.nsplit_s, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
+        } else {
+            cand_stream_kernel<T, D, R><<<dim3(pl.nsplit_s * units), dim3(256), 0, s>>>(
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP, pl.cpb_s,
+                pl.nsplit_s, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        stream_tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(cands, ccount, cmax, pl.nsplit_s * lps,
+                                                              pl.cpb_s * kStreamSlots / lps, d.HQ, pl.nslot, mode,
+                                                              beta,
+                                                              io.tau_hint, io.tau_ref, io.tau, io.support, io.delta,
+                                                              io.supref, sup, supcnt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        support_pv_kernel<T, D, R><<<dim3(kSupSplit, d.HQ, d.B), dim3(256), 0, s>>>(
+            (const T*)v_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP, pl.nslot, sup, supcnt, part3);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        reduce_kernel<<<dim3(d.HQ, d.B), dim3(kReduceThreads), 0, s>>>(part3, d.HQ, D, kSupSplit, io.out);
+        return hipGetLastError();
+    }
+    // softmax: logits with chunk partials, log-partition, PV over every slot
     logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
         (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
         pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, part1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    float* ccand = pl.ncc ? (float*)(ws + pl.off_cand) : nullptr;
-    int32_t* ccnt = pl.ncc ? (int32_t*)(ws + pl.off_ccnt) : nullptr;
-    if (ccand && mode != kModeSoftmax) {
-        cand_kernel<<<dim3(pl.ncc, d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count,
-                                                                  sel_stride, d.G, d.HQ, d.MP, pl.nslot,
-                                                                  pl.nchunk1, alpha, pl.ncc, ccand, ccnt);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    } else {
-        ccand = nullptr;
-    }
-    tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(logits, part1, sl, sel_pages, sel_count, sel_stride,
-                                                     d.G, d.HQ, d.MP, pl.nslot, pl.nchunk1, mode, alpha, beta,
-                                                     io.tau_hint, io.tau_ref, io.tau, io.support, io.delta,
-                                                     io.supref, ccand, ccnt, pl.ncc);
+    softmax_tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(part1, d.HQ, pl.nchunk1, io.tau_ref, io.tau,
+                                                             io.support, io.delta, io.supref);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     pv_kernel<T, D, R><<<dim3(pl.nchunk3, units), dim3(256), 0, s>>>(

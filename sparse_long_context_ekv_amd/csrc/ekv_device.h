@@ -353,6 +353,11 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of ord_key.
+__device__ __forceinline__ float ord_unkey(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 __device__ __forceinline__ int num_pages(int n) { return (n + kPage - 1) / kPage; }
 
 // Sequence length clamped to what its page-table row can address, so that a

@@ -48,15 +48,23 @@ hipError_t launch_select(const Dims& d, int mode, const int32_t* seq_lens, float
 // Decode.
 struct DecodePlan {
     int sparse;      // selection given
-    int fused;       // sparse entmax: logits kernel + one tau/PV kernel per (b, g)
+    int fused;       // sparse entmax within kFusedMaxSlots: logits kernel + one tau/PV kernel per (b, g)
+    int stream;      // entmax otherwise: candidate stream, threshold, PV over the support
+    int nslot;       // slots per (b, h): selected (or all) pages x page size
+    // fused and softmax paths: logits kernel blocks
     int lg_ppb;      // log2 of ppb
-    int nslot;       // logits slots per (b, h)
     int ppb;         // pages per logits block
     int nchunk1;     // logits blocks per (b, g)
+    // softmax path: PV blocks over all slots
     int spb;         // slots per PV block (multiple of 256)
     int nchunk3;     // PV blocks per (b, g)
-    int ncc;         // threshold-candidate chunks per (b, h) (general entmax path), 0 = none
-    size_t off_logits, off_part1, off_part3, off_cand, off_ccnt, bytes;
+    // stream path
+    int cpb_s;       // chunks (of 32 pages) per candidate-stream block
+    int nsplit_s;    // candidate-stream blocks per (b, g)
+    int too_long;    // rows longer than the stream path is built for
+    size_t off_logits, off_part1, off_part3;
+    size_t off_cands, off_ccount, off_cmax, off_sup, off_supcnt;
+    size_t bytes;
 };
 DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha);
 

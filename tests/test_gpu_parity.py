@@ -368,11 +368,12 @@ def _support_slack(s_row, tau, alpha):
                                         ("llama-ragged", 2.0), ("llama-ragged", 4.0 / 3.0), ("llama-ragged", 3.0),
                                         ("flat-long", 1.5), ("long-with-empty", 1.5), ("long-with-empty", 1.0)])
 def test_full_cache_decode(name, alpha):
-    """Full-cache decode (every token) against the oracle.  Rows of more
-    than 4096 slots take the multi-block threshold-candidate compaction
-    (llama-ragged: 5000 tokens), or its fallback when a chunk holds too many
-    candidates (flat-long); an empty sequence gives out 0, tau -inf and
-    support 0 (entmax over no token is undefined)."""
+    """Full-cache decode (every token) against the oracle: the streamed
+    candidate path, several candidate lists per head on the longer rows
+    (llama-ragged: 5000 tokens), and the threshold kernel's list-reading
+    fallback when a head has more than 8192 candidates (flat-long); an empty
+    sequence gives out 0, tau -inf and support 0 (entmax over no token is
+    undefined)."""
     wl = workload(name)
     c = wl.cfg
     out, tau, sup, _, _ = _run_decode(wl, alpha)
@@ -468,6 +469,19 @@ def test_empty_sequence_and_short_sequence():
     q, K, V, n = H.seq_logical(wl, 0)
     ref = oracle.decode.decode(q, K, V, None, 1.5)
     assert np.abs(H.to_np(dec.buf.out[0]) - ref["out"]).max() <= H.OUT_ATOL
+
+
+@pytest.mark.parametrize("name,alpha", [("llama-ragged", 1.5), ("llama-ragged", 2.0), ("long-with-empty", 1.5)])
+def test_full_cache_bitwise_reproducible(name, alpha):
+    """The streamed full-cache path shares its running max between a block's
+    waves through an atomic, so the candidate lists may hold other extra
+    entries from run to run; the results must not change, bit for bit."""
+    wl = workload(name)
+    first = _run_decode(wl, alpha)
+    for _ in range(3):
+        again = _run_decode(wl, alpha)
+        for a, b in zip(first[:3], again[:3]):
+            assert torch.equal(a, b)
 
 
 def test_bitwise_reproducible():
