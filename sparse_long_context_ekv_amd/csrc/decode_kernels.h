@@ -126,9 +126,6 @@ __device__ __forceinline__ void chunk_logits(const Vec<T, D / kRow> (&qv)[R], co
 // wave takes every 4th page of the chunk, UNROLL pages in flight; results
 // go to stage[head * stride + (page - i0) * 16 + token] (-inf past the
 // sequence end or on an unreadable page).  Needs 256-thread blocks.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 // The query operand: lane l holds channels 32 i + 8 (l / 16) .. + 7 of head
 // l % 16 for instruction i (zeros for rows past the group's R heads).
 template <int D, int R>

@@ -21,6 +21,8 @@ namespace ekv {
 typedef uint16_t bf16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef uint8_t fp8_t;        // OCP FP8 E4M3 code (statistics storage only)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));   // a 16x16x32 bf16 MFMA operand (8 per lane)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));     // a 16x16 MFMA accumulator (4 per lane)
 
 constexpr int kPage = 16;     // tokens per page (the only page size built)
 constexpr int kRow = 16;      // lanes per DPP row

@@ -29,8 +29,7 @@
 namespace ekv {
 
 constexpr int kUnroll = 4;
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kMfmaLgPpb = 8;          // pages per matrix-core moments block, at most (256)
 
 // Writes a block's staged results, rows of 2^lg floats in LDS, to output
 // rows starting at column p_begin, np columns of each.  One thread moves four
@@ -243,15 +242,223 @@ __global__ __launch_bounds__(256) void gauss_score_kernel(
     });
 }
 
-// log2 of the pages per block.  Measured on the 128K batched workload: with
-// fp32 statistics (1 KiB per page and group) 256-page blocks, whose staged
-// outputs go out in long runs at the end, beat 16-page blocks by ~3%; with
-// 16-bit statistics (half the bytes per page) the 512 large blocks keep too
-// few loads in flight and 16-page blocks are 25% faster.  Box scores over
-// bf16 min/max on the ragged 64-sequence batch: 64-page blocks 245 us,
-// 16-page 260 us, 256-page 270 us.  Fewer pages when that leaves under 512
-// blocks for 256 CUs or the block's outputs (`out_per_page` floats per page)
-// would pass 64 KiB of LDS.
+// ------------------------------------------------- matrix-core moments ----
+// The Gaussian moments with bf16 queries over 16-bit or FP8 statistics, as
+// small dense contractions on v_mfma_f32_16x16x32_bf16: rows = the group's r
+// query heads (zero-padded to 16), columns = 16 consecutive pages, k = 32
+// channels per instruction.  Every product is exact in the fp32 accumulator:
+//   mu      = q . mean                                  (D/32 instructions)
+//   sigma^2 = (q^2)_hi . var + (q^2)_lo . var, with q^2 (exact in fp32, at
+//             most 16 significant bits) split into two bf16 parts that sum
+//             to it exactly                           (2 D/32 instructions)
+// and FP8 codes widen to bf16 exactly.  The 2r row sums per page of the
+// lane-per-channel kernel above are what limits it on 16-bit statistics
+// (half the bytes per page, the same arithmetic); here a 16-page tile of one
+// group costs 3 D/32 instructions.  (Box scores, q+ . kmax + q- . kmin, ran
+// no faster this way on the ragged batch, 252 us against 245 us: the
+// lane-per-channel box kernel does one select and one packed dot product per
+// channel pair and is not bound by its arithmetic.)
+//
+// Operand layout of the instruction: lane l (t = l % 16, h = l / 16) holds
+// 8 channels of instruction i (mfma_chan) of query head t (A) and of page t
+// (B); the result holds heads 4 h .. 4 h + 3 of page t.  A block covers
+// 2^lg_ppb pages of one sequence and GB groups (GB = 4, 2 or 1, dividing G;
+// grid x = G / GB); wave w takes group w % GB and every (4/GB)-th 16-page
+// tile, kMfmaTiles tiles' loads in flight at once.
+// Measured on the 128K batched workload: bf16 statistics 104-108 us with
+// 256-page blocks (5.0-5.1 TB/s of reads), 112 us with 128, 119 us with 64,
+// 175 us with 16; FP8 54-65 us.  The same kernel with the contractions
+// replaced by a fold of the loaded words runs within 2% of this: the reads
+// (two 256-byte rows per page and group at random physical pages), not the
+// arithmetic, bound it.
+constexpr int kMfmaTiles = 4;
+
+// First channel of lane quarter h's 8-channel slice in instruction i.  The
+// contraction does not depend on which channels an instruction takes, as
+// long as the query and statistics operands agree: 16-bit statistics use
+// 32 i + 8 h (one 16-byte load per instruction), FP8 statistics
+// 64 (i / 2) + 16 h + 8 (i % 2), so one 16-byte load of 16 codes feeds two
+// instructions.
+template <typename S>
+__device__ __forceinline__ int mfma_chan(int i, int h) {
+    return std::is_same<S, fp8_t>::value ? 64 * (i >> 1) + 16 * h + 8 * (i & 1) : 32 * i + 8 * h;
+}
+
+// Sixteen FP8 codes (one 16-byte load) as two bf16 operands, exactly.
+__device__ __forceinline__ void load16_fp8_bf16(const fp8_t* p, bf16x8_t& lo8, bf16x8_t& hi8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const auto f = (k & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)rw[k >> 1], true)
+                               : __builtin_amdgcn_cvt_pk_f32_fp8((int)rw[k >> 1], false);
+        // E4M3 values have 3 fraction bits: the top 16 bits are exact
+        w[k] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    }
+    lo8 = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    hi8 = __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7]));
+}
+
+// Eight bf16 lanes of a query operand from fp32 values that bf16 holds exactly.
+__device__ __forceinline__ bf16x8_t pack8_bf16(const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = (__float_as_uint(v[2 * k]) >> 16) | (__float_as_uint(v[2 * k + 1]) & 0xffff0000u);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+template <typename S, int D, int R, int GB>
+__global__ __launch_bounds__(256) void gauss_mfma_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const S* __restrict__ kmean, const S* __restrict__ kvar, float* __restrict__ mu, float* __restrict__ sigma,
+    int G, int MP, int NP, int lg_ppb, float inv_sqrt_d, float inv_d, bool vec) {
+    constexpr int NT = D / 32;
+    static_assert(NT % 2 == 0, "FP8 statistics feed instructions in pairs");
+    static_assert(std::is_same<S, bf16_t>::value || std::is_same<S, fp8_t>::value, "16-bit or FP8 statistics");
+    extern __shared__ float stage[];               // [2][GB*R][ppb]: mu, then sigma
+    const int ppb = 1 << lg_ppb;
+    const int b = blockIdx.z, g0 = blockIdx.x * GB;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const int p_begin = blockIdx.y * ppb;
+    if (p_begin >= M) return;                      // block-uniform
+    const int p_end = min(M, p_begin + ppb);
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+    const int gl = wv % GB, g = g0 + gl;
+    const int HQ = G * R;
+
+    // the query operands of this wave's group (rows past R are zero)
+    bf16x8_t qa[3][NT];                            // q, (q^2)_hi, (q^2)_lo
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        float v[8];
+        const uint4 raw = tq < R ? *reinterpret_cast<const uint4*>(q + ((size_t)b * HQ + g * R + tq) * D +
+                                                                   mfma_chan<S>(i, hq))
+                                 : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(rw[k] << 16);
+            v[2 * k + 1] = __uint_as_float(rw[k] & 0xffff0000u);
+        }
+        float hi[8], lo[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float q2 = v[k] * v[k];                                       // exact
+            hi[k] = __uint_as_float(__float_as_uint(q2) & 0xffff0000u);         // top 8 significant bits
+            lo[k] = q2 - hi[k];                                                 // the rest, exact in bf16
+        }
+        qa[0][i] = pack8_bf16(v);
+        qa[1][i] = pack8_bf16(hi);
+        qa[2][i] = pack8_bf16(lo);
+    }
+
+    // the block's table entries, read once (-1: past the block or outside the cache)
+    __shared__ int sh_phys[1 << kMfmaLgPpb];
+    const int32_t* pt = page_table + (size_t)b * MP;
+    for (int t = threadIdx.x; t < ppb; t += blockDim.x) {
+        const int ph = p_begin + t < p_end ? pt[p_begin + t] : -1;
+        sh_phys[t] = ph >= 0 && ph < NP ? ph : -1;
+    }
+    __syncthreads();
+    const int ntile = (p_end - p_begin + kPage - 1) / kPage;
+    constexpr int WPG = 4 / GB;                     // waves per group
+    for (int t0 = wv / GB; t0 < ntile; t0 += WPG * kMfmaTiles) {   // wave-uniform
+        bf16x8_t s0[kMfmaTiles][NT], s1[kMfmaTiles][NT];
+        bool ok[kMfmaTiles];
+        // every tile's loads first, without branches (a page past the block
+        // or with a bad table entry reads page 0 and is ignored)
+#pragma unroll
+        for (int u = 0; u < kMfmaTiles; ++u) {
+            const int pi = (t0 + u * WPG) * kPage + tq;   // page within the block
+            const int ph = sh_phys[pi < ppb ? pi : 0];
+            ok[u] = pi < ppb && ph >= 0;
+            const size_t off = ((size_t)(ok[u] ? ph : 0) * G + g) * D;
+            if constexpr (std::is_same<S, fp8_t>::value) {
+#pragma unroll
+                for (int i = 0; i < NT; i += 2) {
+                    load16_fp8_bf16(kmean + off + mfma_chan<S>(i, hq), s0[u][i], s0[u][i + 1]);
+                    load16_fp8_bf16(kvar + off + mfma_chan<S>(i, hq), s1[u][i], s1[u][i + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    s0[u][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kmean + off + mfma_chan<S>(i, hq)));
+                    s1[u][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kvar + off + mfma_chan<S>(i, hq)));
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kMfmaTiles; ++u) {
+            const int tile = t0 + u * WPG;
+            if (tile < ntile) {                                       // wave-uniform
+                const int p = p_begin + tile * kPage + tq;
+                f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][i], s0[u][i], a0, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][i], s1[u][i], a1, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][i], s1[u][i], a1, 0, 0, 0);
+                }
+                if (p < p_end) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int head = 4 * hq + j;
+                        if (head < R) {
+                            // bad table entry: mu = -inf, sigma = 0 (a point mass that adds nothing)
+                            stage[(gl * R + head) * ppb + p - p_begin] = ok[u] ? a0[j] * inv_sqrt_d : -INFINITY;
+                            stage[((GB + gl) * R + head) * ppb + p - p_begin] =
+                                ok[u] ? sqrtf(fmaxf(a1[j], 0.0f) * inv_d) : 0.0f;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    flush_rows(stage, 2 * GB * R, lg_ppb, p_begin, p_end - p_begin, vec, [&](int rr) {
+        return rr < GB * R ? mu + ((size_t)b * HQ + g0 * R + rr) * MP
+                           : sigma + ((size_t)b * HQ + g0 * R + rr - GB * R) * MP;
+    });
+}
+
+template <typename S, int D, int R>
+static hipError_t run_gauss_mfma(const Dims& d, const void* q, const int32_t* pt, const int32_t* sl,
+                                 const void* kmean, const void* kvar, float* mu, float* sigma, hipStream_t s) {
+    const int GB = d.G % 4 == 0 ? 4 : (d.G % 2 == 0 ? 2 : 1);
+    // (all G groups of a page in one 8-wave block measured slower than two
+    // 4-group blocks side by side)
+    int lg = kMfmaLgPpb;
+    // at most 32 KiB of staged outputs, and at least 1024 blocks where the batch allows
+    while (lg > 4 && ((((size_t)2 * GB * R) << lg) * sizeof(float) > 32768 ||
+                      (((long)d.B * d.MP) >> lg) * (d.G / GB) < 1024))
+        --lg;
+    const size_t lds = (((size_t)2 * GB * R) << lg) * sizeof(float);
+    // group blocks of the same pages side by side in launch order: the G rows
+    // of a physical page's statistics are adjacent in memory
+    const dim3 grid(d.G / GB, (d.MP + (1 << lg) - 1) >> lg, d.B);
+    const bool vec = d.MP % 4 == 0 && ((uintptr_t)mu & 15) == 0 && ((uintptr_t)sigma & 15) == 0;
+#define EKV_LAUNCH_MFMA(GBV)                                                                                      \
+    gauss_mfma_kernel<S, D, R, GBV><<<grid, dim3(256), lds, s>>>((const bf16_t*)q, pt, sl, (const S*)kmean,       \
+                                                                 (const S*)kvar, mu, sigma, d.G, d.MP, d.NP, lg,  \
+                                                                 1.0f / sqrtf((float)D), 1.0f / (float)D, vec)
+    if (GB == 4) EKV_LAUNCH_MFMA(4);
+    else if (GB == 2) EKV_LAUNCH_MFMA(2);
+    else EKV_LAUNCH_MFMA(1);
+#undef EKV_LAUNCH_MFMA
+    return hipGetLastError();
+}
+
+// log2 of the pages per block of the lane-per-channel kernels.  Measured on
+// the 128K batched workload: with fp32 statistics (1 KiB per page and group)
+// 256-page blocks, whose staged outputs go out in long runs at the end, beat
+// 16-page blocks by ~3%; with 16-bit statistics (half the bytes per page)
+// the 512 large blocks keep too few loads in flight and 16-page blocks are
+// 25% faster.  Box scores over bf16 min/max on the ragged 64-sequence batch:
+// 64-page blocks 245 us, 16-page 260 us, 256-page 270 us.  (bf16 queries
+// over 16-bit or FP8 statistics now take the matrix-core kernels.)  Fewer
+// pages when that leaves under 512 blocks for 256 CUs or the block's outputs
+// (`out_per_page` floats per page) would pass 64 KiB of LDS.
 static int score_lg_ppb(const Dims& d, int out_per_page, int lg_max) {
     const long units = (long)d.B * d.MP;
     int lg = lg_max;
@@ -329,11 +536,13 @@ hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_
                               const int32_t* seq_lens, const void* kmean, const void* kvar,
                               float* mu, float* sigma, hipStream_t s) {
 #define EKV_GS(RR, T, S, DD) return run_gauss<T, S, DD, RR>(d, q, page_table, seq_lens, kmean, kvar, mu, sigma, s)
+#define EKV_GSM(RR, S, DD) \
+    return run_gauss_mfma<S, DD, RR>(d, q, page_table, seq_lens, kmean, kvar, mu, sigma, s)
     if (d.kv_bf16) {
         if (d.stat == kStatBF16) {
-            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, bf16_t, 64) }
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GSM, bf16_t, 128) } else { EKV_R_SWITCH(EKV_GSM, bf16_t, 64) }
         } else if (d.stat == kStatFP8) {
-            if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, fp8_t, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, fp8_t, 64) }
+            if (d.D == 128) { EKV_R_SWITCH(EKV_GSM, fp8_t, 128) } else { EKV_R_SWITCH(EKV_GSM, fp8_t, 64) }
         } else {
             if (d.D == 128) { EKV_R_SWITCH(EKV_GS, bf16_t, float, 128) } else { EKV_R_SWITCH(EKV_GS, bf16_t, float, 64) }
         }
@@ -347,6 +556,7 @@ hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_
         }
     }
 #undef EKV_GS
+#undef EKV_GSM
 }
 
 }  // namespace ekv

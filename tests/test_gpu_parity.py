@@ -245,6 +245,42 @@ def test_gauss_moments(stat):
         np.testing.assert_allclose(H.to_np(sg[b, :, :M]), osg, rtol=tol, atol=tol * np.abs(osg).max())
 
 
+@pytest.mark.parametrize("heads,groups,dim,stat", [(8, 8, 128, "bf16"), (16, 8, 128, "fp8"), (64, 8, 128, "bf16"),
+                                                   (32, 8, 64, "bf16"), (32, 8, 64, "fp8"), (12, 6, 128, "bf16"),
+                                                   (8, 1, 64, "fp8")])
+def test_gauss_moments_16bit_shapes(heads, groups, dim, stat):
+    """bf16 queries over 16-bit / FP8 statistics take the matrix-core moments
+    kernel: every r (1, 2, 8 heads per group), d = 64, group counts that
+    split the block 4, 2 or 1 ways, a ragged batch whose lengths end inside
+    a 16-page tile, and one page-table entry outside the cache (mu = -inf,
+    sigma = 0 there); against the oracle on the stored statistics at 1e-5."""
+    cfg = W.CONFIGS[3].scaled(batch=3, num_q_heads=heads, num_kv_groups=groups, head_dim=dim)
+    wl = W.make_workload(cfg, "cuda", seq_lens=[1111, 4099, 37])
+    c = wl.cfg
+    st = _stats(wl, stat)
+    pt = wl.page_table.clone()
+    pt[1, 7] = wl.num_phys + 5                       # outside the cache
+    mu = torch.empty(c.batch, c.num_q_heads, wl.max_pages, device="cuda")
+    sg = torch.empty_like(mu)
+    ekv.score_pages(_shape(wl, stat), ekv.SEL_GAUSS, wl.q, pt, wl.seq_lens, kmean=st["kmean"], kvar=st["kvar"],
+                    mu=mu, sigma=sg)
+    H.sync()
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        mean, var = _stored_stats_logical(st, wl, b)
+        omu, osg = oracle.paged.gauss_moments(q, mean, var)
+        M = omu.shape[1]
+        gmu, gsg = H.to_np(mu[b, :, :M]), H.to_np(sg[b, :, :M])
+        if b == 1:
+            assert np.all(gmu[:, 7] == -np.inf) and np.all(gsg[:, 7] == 0.0)
+            keep = np.ones(M, dtype=bool)
+            keep[7] = False
+            gmu, gsg, omu, osg = gmu[:, keep], gsg[:, keep], omu[:, keep], osg[:, keep]
+        tol = 1e-5
+        np.testing.assert_allclose(gmu, omu, rtol=tol, atol=tol * np.abs(omu).max())
+        np.testing.assert_allclose(gsg, osg, rtol=tol, atol=tol * np.abs(osg).max())
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama-ragged"])
 def test_topk_selection(name):
     wl = workload(name)
