@@ -59,7 +59,7 @@
 #include <stdint.h>
 
 /* ABI version of this header (ekv_abi_version() returns it). */
-#define EKV_ABI_VERSION 5
+#define EKV_ABI_VERSION 6
 
 #ifdef __cplusplus
 extern "C" {
@@ -150,14 +150,20 @@ ekv_status ekv_append_kv(const ekv_shape* shape, const void* k_new, const void* 
  *   sigma_{h,p} = sqrt((1/D) sum_i q_{h,i}^2 kvar_{p,i})
  *   (per-head moments of the page's token scores, channels treated as
  *   independent).
+ * head_score [B][HQ][MP] fp32 (NULL ok; EKV_SEL_TOPK only, else
+ *   EKV_ERR_INVALID_ARG): the per-head box scores u_{h,p} before the pooling
+ *   over the group's heads, for inspection (a second, unoptimised launch;
+ *   score_{g,p} = max over the group's heads of them, up to fp32 rounding).
  * Entries for p >= M_b are not written.  A page p < M_b whose page_table
- * entry lies outside [0, NP) is not read: it gets score -inf, or mu -inf and
- * sigma 0 (a point mass below every threshold).  Accumulation is fp32.     */
+ * entry lies outside [0, NP) is not read: it gets score -inf (head_score
+ * likewise), or mu -inf and sigma 0 (a point mass below every threshold).
+ * Accumulation is fp32.                                                    */
 ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void* q,
                            const int32_t* page_table, const int32_t* seq_lens,
                            const void* kmin, const void* kmax,
                            const void* kmean, const void* kvar,
-                           float* score, float* mu, float* sigma, void* stream);
+                           float* score, float* mu, float* sigma, float* head_score,
+                           void* stream);
 
 /* Candidate page selection, one page set per (sequence, KV group)
  * ([EKV] section 4.3; Appendix B.2).

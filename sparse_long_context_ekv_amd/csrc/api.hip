@@ -167,18 +167,22 @@ ekv_status ekv_append_kv(const ekv_shape* shape, const void* k_new, const void* 
 
 ekv_status ekv_score_pages(const ekv_shape* shape, int32_t selector, const void* q, const int32_t* page_table,
                            const int32_t* seq_lens, const void* kmin, const void* kmax, const void* kmean,
-                           const void* kvar, float* score, float* mu, float* sigma, void* stream) {
+                           const void* kvar, float* score, float* mu, float* sigma, float* head_score,
+                           void* stream) {
     ekv::Dims d;
     ekv_status st = check_shape(shape, &d);
     if (st != EKV_OK) return st;
     if (!q || !page_table || !seq_lens) return fail(EKV_ERR_INVALID_ARG, "q, page_table and seq_lens are required");
     if (selector == EKV_SEL_TOPK) {
         if (!kmin || !kmax || !score) return fail(EKV_ERR_INVALID_ARG, "top-k scoring needs kmin, kmax and score");
-        return hip_status(ekv::launch_box_score(d, q, page_table, seq_lens, kmin, kmax, score, (hipStream_t)stream),
-                          "ekv_score_pages");
+        hipError_t e = ekv::launch_box_score(d, q, page_table, seq_lens, kmin, kmax, score, (hipStream_t)stream);
+        if (e == hipSuccess && head_score)
+            e = ekv::launch_head_box_score(d, q, page_table, seq_lens, kmin, kmax, head_score, (hipStream_t)stream);
+        return hip_status(e, "ekv_score_pages");
     }
     if (selector == EKV_SEL_GAUSS) {
         if (!kmean || !kvar || !mu || !sigma) return fail(EKV_ERR_INVALID_ARG, "Gaussian scoring needs kmean, kvar, mu and sigma");
+        if (head_score) return fail(EKV_ERR_INVALID_ARG, "head_score is an output of top-k scoring only");
         return hip_status(ekv::launch_gauss_score(d, q, page_table, seq_lens, kmean, kvar, mu, sigma,
                                                   (hipStream_t)stream),
                           "ekv_score_pages");

@@ -31,6 +31,8 @@ hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new,
 hipError_t launch_box_score(const Dims& d, const void* q, const int32_t* page_table,
                             const int32_t* seq_lens, const void* kmin, const void* kmax,
                             float* score, hipStream_t s);
+hipError_t launch_head_box_score(const Dims& d, const void* q, const int32_t* page_table, const int32_t* seq_lens,
+                                 const void* kmin, const void* kmax, float* head_score, hipStream_t s);
 hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_table,
                               const int32_t* seq_lens, const void* kmean, const void* kvar,
                               float* mu, float* sigma, hipStream_t s);

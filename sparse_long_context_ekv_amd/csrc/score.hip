@@ -532,6 +532,60 @@ hipError_t launch_box_score(const Dims& d, const void* q, const int32_t* page_ta
 #undef EKV_BOX
 }
 
+// Per-head box scores u_{h,p} before the pooling over the group's heads (an
+// optional output of top-k scoring, for inspection; not on the step's path):
+// one 16-lane row per page, every head of the batch row in turn, fp32 sums.
+// Pages past the sequence end are not written; an unreadable table entry
+// gives -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void head_box_kernel(const T* __restrict__ q, const int32_t* __restrict__ page_table,
+                                                       const int32_t* __restrict__ seq_lens, const T* __restrict__ kmin,
+                                                       const T* __restrict__ kmax, float* __restrict__ head_score,
+                                                       int HQ, int G, int MP, int NP, float inv_sqrt_d) {
+    constexpr int CH = D / kRow;
+    const int b = blockIdx.y;
+    const int M = num_pages(seq_len_at(seq_lens, b, MP));
+    const int p = blockIdx.x * kRow + (threadIdx.x >> 4);
+    const int lane = threadIdx.x & (kRow - 1);
+    if (blockIdx.x * kRow >= M) return;            // block-uniform
+    const bool live = p < M;                        // rows past the end still take part in the row sums
+    const int ph = live ? page_table[(size_t)b * MP + p] : -1;
+    const bool ok = ph >= 0 && ph < NP;
+    const int R = HQ / G;
+    for (int h = 0; h < HQ; ++h) {
+        const int g = h / R;
+        Vec<T, CH> qv, lo, hi;
+        qv.load(q + ((size_t)b * HQ + h) * D + lane * CH);
+        const size_t off = ((size_t)(ok ? ph : 0) * G + g) * D + lane * CH;
+        lo.load(kmin + off);
+        hi.load(kmax + off);
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const float qc = qv.get(c);
+            acc += fmaxf(qc * hi.get(c), qc * lo.get(c));
+        }
+        acc = row_sum16(acc);
+        if (live && lane == 0) head_score[((size_t)b * HQ + h) * MP + p] = ok ? acc * inv_sqrt_d : -INFINITY;
+    }
+}
+
+hipError_t launch_head_box_score(const Dims& d, const void* q, const int32_t* page_table, const int32_t* seq_lens,
+                                 const void* kmin, const void* kmax, float* head_score, hipStream_t s) {
+    const dim3 grid((d.MP + kRow - 1) / kRow, d.B);
+    const float isd = 1.0f / sqrtf((float)d.D);
+#define EKV_HB(T, DD)                                                                                              \
+    head_box_kernel<T, DD><<<grid, dim3(256), 0, s>>>((const T*)q, page_table, seq_lens, (const T*)kmin,          \
+                                                      (const T*)kmax, head_score, d.HQ, d.G, d.MP, d.NP, isd)
+    if (d.kv_bf16) {
+        if (d.D == 128) EKV_HB(bf16_t, 128); else EKV_HB(bf16_t, 64);
+    } else {
+        if (d.D == 128) EKV_HB(float, 128); else EKV_HB(float, 64);
+    }
+#undef EKV_HB
+    return hipGetLastError();
+}
+
 hipError_t launch_gauss_score(const Dims& d, const void* q, const int32_t* page_table,
                               const int32_t* seq_lens, const void* kmean, const void* kvar,
                               float* mu, float* sigma, hipStream_t s) {

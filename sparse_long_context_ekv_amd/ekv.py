@@ -61,7 +61,7 @@ def load(path: str | None = None):
     sp = ctypes.POINTER(Shape)
     lib.ekv_build_page_stats.argtypes = [sp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_append_kv.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-    lib.ekv_score_pages.argtypes = [sp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.ekv_score_pages.argtypes = [sp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.ekv_select.argtypes = [sp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
     lib.ekv_entmax_decode.argtypes = [sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp]
@@ -129,10 +129,10 @@ def append_kv(shape, k_new, v_new, page_table, seq_lens, k_cache, v_cache, kmin=
 
 
 def score_pages(shape, selector, q, page_table, seq_lens, kmin=None, kmax=None, kmean=None, kvar=None,
-                score=None, mu=None, sigma=None, stream=None):
+                score=None, mu=None, sigma=None, stream=None, head_score=None):
     _check(load().ekv_score_pages(ctypes.byref(shape), int(selector), _ptr(q), _ptr(page_table), _ptr(seq_lens),
                                   _ptr(kmin), _ptr(kmax), _ptr(kmean), _ptr(kvar), _ptr(score), _ptr(mu),
-                                  _ptr(sigma), _stream(stream)))
+                                  _ptr(sigma), _ptr(head_score), _stream(stream)))
 
 
 def select_workspace_bytes(shape, selector, alpha=1.5, budget_pages=1, z=3.0) -> int:

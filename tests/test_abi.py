@@ -37,7 +37,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ekv_abi_version() == 5
+    assert lib.ekv_abi_version() == 6
 
 
 def _shape(**kw):
@@ -80,11 +80,12 @@ def test_null_required_pointers_rejected_before_launch(lib):
     assert st == ekv.ERR_INVALID_ARG
     st = lib.ekv_build_page_stats(ctypes.byref(sh), 8, 8, 8, None, 0, 8, None, None, None, None)
     assert st == ekv.ERR_INVALID_ARG                       # kmin without kmax
-    st = lib.ekv_score_pages(ctypes.byref(sh), ekv.SEL_TOPK, 8, 8, 8, None, None, None, None, None, None, None, None)
+    st = lib.ekv_score_pages(ctypes.byref(sh), ekv.SEL_TOPK, 8, 8, 8, None, None, None, None, None, None, None, None,
+                             None)
     assert st == ekv.ERR_INVALID_ARG
-    st = lib.ekv_score_pages(ctypes.byref(sh), 5, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None)
+    st = lib.ekv_score_pages(ctypes.byref(sh), 5, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None, None)
     assert st == ekv.ERR_INVALID_ARG
-    assert lib.ekv_score_pages(None, 0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None) == ekv.ERR_INVALID_ARG
+    assert lib.ekv_score_pages(None, 0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 8, None, None) == ekv.ERR_INVALID_ARG
 
 
 def test_select_argument_checks(lib):

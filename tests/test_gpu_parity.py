@@ -185,6 +185,40 @@ def test_box_scores(name):
         assert bool((score[b, :, M:] == -7.0).all())                   # past the end: untouched
 
 
+@pytest.mark.parametrize("name", ["tiny", "llama-ragged"])
+def test_per_head_box_scores(name):
+    """The optional per-head box scores of top-k scoring: u_{h,p} against the
+    oracle, their maximum over a group's heads against the pooled score, -inf
+    at a page whose table entry lies outside the cache, nothing written past
+    a sequence's last page."""
+    wl = workload(name)
+    c = wl.cfg
+    st = _stats(wl)
+    pt = wl.page_table.clone()
+    pt[0, 1] = -3                                                     # outside the cache
+    score = torch.full((c.batch, c.num_kv_groups, wl.max_pages), -7.0, device="cuda")
+    hs = torch.full((c.batch, c.num_q_heads, wl.max_pages), -7.0, device="cuda")
+    ekv.score_pages(_shape(wl), ekv.SEL_TOPK, wl.q, pt, wl.seq_lens, kmin=st["kmin"], kmax=st["kmax"], score=score,
+                    head_score=hs)
+    H.sync()
+    r = c.num_q_heads // c.num_kv_groups
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        kmin, kmax, _, _ = oracle.paged.page_stats(K, P)
+        u, U = oracle.paged.box_scores(q, kmin, kmax)
+        M = u.shape[1]
+        got = H.to_np(hs[b, :, :M])
+        pooled = H.to_np(score[b, :, :M])
+        keep = np.ones(M, dtype=bool)
+        if b == 0 and M > 1:
+            assert np.all(got[:, 1] == -np.inf) and np.all(pooled[:, 1] == -np.inf)
+            keep[1] = False
+        np.testing.assert_allclose(got[:, keep], u[:, keep], rtol=1e-5, atol=1e-5 * np.abs(u).max())
+        gmax = got.reshape(c.num_kv_groups, r, M).max(axis=1)
+        np.testing.assert_allclose(gmax[:, keep], pooled[:, keep], rtol=1e-5, atol=1e-5 * np.abs(U).max())
+        assert bool((hs[b, :, M:] == -7.0).all())                      # past the end: untouched
+
+
 def test_scores_with_bad_table_entries():
     """A page inside a sequence whose page-table entry lies outside [0, NP)
     is never read: its box score is -inf and its moments are mu = -inf,
