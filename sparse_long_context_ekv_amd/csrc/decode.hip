@@ -16,7 +16,9 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     pl.fused = sparse && alpha > 1.0f && pl.nslot <= kFusedMaxSlots;
     pl.stream = !pl.fused && alpha > 1.0f;
     const size_t bh = (size_t)d.B * d.HQ;
-    pl.lg_ppb = sparse ? 3 : 5;
+    // pages per logits block: 64 for the fused path's bf16 keys (8-wave
+    // blocks on the matrix cores), 8 for other selections, 32 over the cache
+    pl.lg_ppb = pl.fused && d.kv_bf16 ? 6 : (sparse ? 3 : 5);
     pl.ppb = 1 << pl.lg_ppb;
     pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
     if (pl.nchunk1 < 1) pl.nchunk1 = 1;

@@ -37,7 +37,7 @@ namespace ekv {
 
 enum { kModeSoftmax = 0, kModeBeta1 = 1, kModeBeta2 = 2, kModeGeneral = 3 };
 constexpr int kLogitUnroll = 4;
-constexpr int kMaxLogitPpb = 32;       // pages per logits block at most (plan_decode: 8 or 32)
+constexpr int kMaxLogitPpb = 64;       // pages per logits block at most (plan_decode: 8, 32 or 64)
 constexpr int kCandCap = 8192;        // threshold candidates per head gathered in LDS (streamed path)
 
 // -------------------------------------------------------------- logits ----
@@ -143,12 +143,12 @@ struct MfmaQ {
     }
 };
 
-// UNROLL pages of one wave in registers: pages i, i + 4, ..., i + 4 (UNROLL
-// - 1) of the chunk [i0, i1).  load() issues every read without branches (a
+// UNROLL pages of one wave in registers: pages i, i + NW, ..., i + NW (UNROLL
+// - 1) of the chunk [i0, i1), NW = the waves that share the chunk.  load() issues every read without branches (a
 // page past the chunk or unreadable reads page 0 and is ignored); logits()
 // contracts them with the query tile and writes stage[head * stride +
 // (page - i0) * 16 + token].
-template <int D, int UNROLL>
+template <int D, int UNROLL, int NW = 4>
 struct MfmaKPages {
     bf16x8_t kb[UNROLL][D / 32];
     bool ok[UNROLL];
@@ -159,7 +159,7 @@ struct MfmaKPages {
         const int l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int ii = i + 4 * u;
+            const int ii = i + NW * u;
             const int t = ii < i1 ? ii - i0 : 0;
             const int ph = sh_phys[t];
             lp[u] = sh_lp[t];
@@ -190,7 +190,7 @@ struct MfmaKPages {
         const int l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int ii = i + 4 * u;
+            const int ii = i + NW * u;
             if (ii < i1) {                                          // wave-uniform
                 f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -208,23 +208,28 @@ struct MfmaKPages {
     }
 };
 
-template <int D, int R, int UNROLL>
+template <int D, int R, int UNROLL, int NW = 4>
 __device__ __forceinline__ void chunk_logits_mfma(const bf16_t* __restrict__ qrow, const bf16_t* __restrict__ k_cache,
                                                   const int* sh_lp, const int* sh_phys, int i0, int i1, int n, int G,
                                                   int g, float inv_sqrt_d, float* stage, int stride) {
     MfmaQ<D, R> qa;
     qa.load(qrow);
-    for (int i = i0 + (int)(threadIdx.x >> 6); i < i1; i += 4 * UNROLL) {     // wave-uniform
-        MfmaKPages<D, UNROLL> kp;
+    for (int i = i0 + (int)(threadIdx.x >> 6); i < i1; i += NW * UNROLL) {    // wave-uniform
+        MfmaKPages<D, UNROLL, NW> kp;
         kp.load(k_cache, sh_lp, sh_phys, i, i0, i1, G, g);
         kp.template logits<R>(qa, i, i0, i1, n, inv_sqrt_d, stage, stride);
     }
 }
 
 // PART: also keep per-chunk (max, sum exp(s - max), valid count) per head,
-// which the general threshold kernel reads (softmax, full cache).
-template <typename T, int D, int R, bool PART>
-__global__ __launch_bounds__(256) void logits_kernel(
+// which the general threshold kernel reads (softmax, full cache).  NWV: waves
+// per block; 8 (64 pages, four per wave per round on the matrix cores, two
+// blocks per CU) only for bf16 keys without partials, so that the selected
+// logits of a 128-unit batch take one round of blocks: a block's time is its
+// chain of dependent loads (selection -> page table -> K tile), and 64 pages
+// per block amortise it.
+template <typename T, int D, int R, bool PART, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void logits_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
     const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int lg_ppb,
@@ -265,9 +270,10 @@ __global__ __launch_bounds__(256) void logits_kernel(
     }
     __syncthreads();
 
+    static_assert(NWV == 4 || (!PART && std::is_same<T, bf16_t>::value), "8-wave blocks: bf16 keys, no partials");
     if constexpr (!PART && std::is_same<T, bf16_t>::value) {
-        chunk_logits_mfma<D, R, 2>(q + ((size_t)b * HQ + g * R) * D, k_cache, sh_lp, sh_phys, i0, i1, n, G, g,
-                                   inv_sqrt_d, stage, ppb * kPage);
+        chunk_logits_mfma<D, R, (NWV == 4 ? 2 : 4), NWV>(q + ((size_t)b * HQ + g * R) * D, k_cache, sh_lp, sh_phys,
+                                                          i0, i1, n, G, g, inv_sqrt_d, stage, ppb * kPage);
     } else {
         chunk_logits<T, D, R, PART>(qv, k_cache, sh_lp, sh_phys, i0, i1, ppb, n, G, g, lane, row, inv_sqrt_d, st,
                                     run_m, run_l, run_c);
@@ -1767,9 +1773,15 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
     const int units = d.B * d.G;
     const size_t lds = ((size_t)R * pl.ppb * kPage) * sizeof(float);
     if (pl.fused) {
-        logits_kernel<T, D, R, false><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
-            (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
-            pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            logits_kernel<T, D, R, false, 8><<<dim3(pl.nchunk1, units), dim3(512), lds, s>>>(
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
+                pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
+        } else {
+            logits_kernel<T, D, R, false><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
+                pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         switch (mode) {
