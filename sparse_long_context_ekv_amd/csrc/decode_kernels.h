@@ -486,6 +486,9 @@ constexpr int kStreamSlots = kStreamPpb * kPage;      // 512 slots per chunk
 constexpr int kStreamMaxChunks = 64;                  // chunks per candidate-stream block at most
 constexpr int kStreamMaxLists = 2048;                 // candidate lists per (b, h) at most (4 per block)
 constexpr int kStreamStage = 1024;                    // candidates staged in LDS per wave (bf16 stream)
+constexpr int kTauT = 512;                            // threads of the streamed threshold kernel (2 blocks per CU)
+constexpr int kTauWaveCands = 2048;                   // at most this many candidates: one wave iterates
+constexpr int kTauW = kTauT / 64;
 constexpr int kStreamBlocks = 512;                    // aim: about this many candidate-stream blocks (2 per CU)
 constexpr int kSupSplit = 8;                          // PV blocks per head over its support
 constexpr int kStreamUnroll = 8;                      // pages' tiles in flight per row while streaming
@@ -768,19 +771,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
 }
 
-static __global__ __launch_bounds__(256) void stream_tau_kernel(
+template <int MODE>
+static __global__ __launch_bounds__(kTauT) void stream_tau_kernel(
     const float2* __restrict__ cands, const int32_t* __restrict__ ccount, const float* __restrict__ cmax,
-    int nsplit, int lcap, int HQ, int nslot, int mode, float beta, const float* __restrict__ tau_hint,
+    int nsplit, int lcap, int HQ, int nslot, float beta, const float* __restrict__ tau_hint,
     const float* __restrict__ tau_ref, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
     float* __restrict__ delta_out, int32_t* __restrict__ supref_out, float2* __restrict__ sup_list,
     int32_t* __restrict__ sup_count) {
+    constexpr int mode = MODE;                            // compile-time: no powf where beta is 1 or 2
     constexpr int UNR = 8;                                // flat entries in flight per thread
     __shared__ float cand[kCandCap];
     __shared__ float cslot[kCandCap];                     // slot bits of each candidate
     __shared__ int loff[kStreamMaxLists + 1];             // flat offset of each list
-    __shared__ float red[8];
-    __shared__ int wsum[8];
-    __shared__ float red5[2][4][5];
+    __shared__ float red[2 * kTauW];
+    __shared__ int wsum[2 * kTauW];
+    __shared__ float red5[2][kTauW][5];
     int phase = 0, p5 = 0;
     const int h = blockIdx.x, b = blockIdx.y;
     const size_t oh = (size_t)b * HQ + h;
@@ -788,8 +793,8 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
     const int32_t* counts = ccount + oh * nsplit;
 
     float xmax = -INFINITY;
-    for (int c = threadIdx.x; c < nsplit; c += 256) xmax = fmaxf(xmax, cmax[oh * nsplit + c]);
-    xmax = block_max<4>(xmax, red, phase);
+    for (int c = threadIdx.x; c < nsplit; c += kTauT) xmax = fmaxf(xmax, cmax[oh * nsplit + c]);
+    xmax = block_max<kTauW>(xmax, red, phase);
     if (!(xmax > -INFINITY)) {                             // no valid token
         if (threadIdx.x == 0) {
             tau_out[oh] = -INFINITY;
@@ -804,14 +809,14 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
 
     // Flat offsets of the lists: thread t scans splits [t*per, (t+1)*per).
     {
-        const int per = (nsplit + 255) / 256;
+        const int per = (nsplit + kTauT - 1) / kTauT;
         int local = 0;
         for (int i = 0; i < per; ++i) {
             const int c = threadIdx.x * per + i;
             local += c < nsplit ? counts[c] : 0;
         }
         int ex, ex2, tot, tot2;
-        block_excl_scan2<4>(local, 0, ex, ex2, &tot, &tot2, wsum);
+        block_excl_scan2<kTauW>(local, 0, ex, ex2, &tot, &tot2, wsum);
         for (int i = 0; i < per; ++i) {
             const int c = threadIdx.x * per + i;
             if (c < nsplit) {
@@ -823,16 +828,16 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
         __syncthreads();
     }
     const int T = loff[nsplit];
-    // Every list entry, by flat index f = tid, tid + 256, ... (UNR loads in
+    // Every list entry, by flat index f = tid, tid + kTauT, ... (UNR loads in
     // flight), in a fixed order: fn(x, slot bits).
     auto each_flat = [&](auto&& fn) {
         int sidx = 0;                                      // list of the current f, moved forward
-        for (int f0 = threadIdx.x; f0 < T; f0 += 256 * UNR) {
+        for (int f0 = threadIdx.x; f0 < T; f0 += kTauT * UNR) {
             float2 e[UNR];
             bool ok[UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int f = f0 + u * 256;
+                const int f = f0 + u * kTauT;
                 ok[u] = f < T;
                 const int ff = ok[u] ? f : T - 1;        // past the end: the last entry (ignored); keeps sidx monotone
                 while (loff[sidx + 1] <= ff) ++sidx;
@@ -844,48 +849,48 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
         }
     };
     // Candidates x > lo into LDS in one pass over the lists: rounds of
-    // 256 * GUNR entries (all in flight at once; entry f0 + 256 u + t read by
+    // kTauT * GUNR entries (all in flight at once; entry f0 + kTauT u + t read by
     // thread t), each candidate placed at its rank in flat order: the
     // candidates of earlier rounds, of the round's earlier u, of earlier
     // waves at this u, and of lower lanes (wave ballot).  So they land in
     // list order and, within a list, in slot order, whatever else the lists
     // hold: the set x > lo and that order fix every sum below.  If they do
     // not all fit, the later passes read the lists instead.
-    constexpr int GUNR = 16;                              // GUNR * 4 (u, wave) pairs: one per lane of a wave
-    __shared__ int gbase[GUNR * 4 + 1];                   // per (u, wave): rank of its first candidate; round total
+    constexpr int GUNR = 64 / kTauW;                      // GUNR * kTauW (u, wave) pairs: one per lane of a wave
+    __shared__ int gbase[GUNR * kTauW + 1];               // per (u, wave): rank of its first candidate; round total
     int total = 0;
     {
         const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
         int sidx = 0;
-        for (int f0 = 0; f0 < T; f0 += 256 * GUNR) {      // block-uniform
+        for (int f0 = 0; f0 < T; f0 += kTauT * GUNR) {    // block-uniform
             float2 e[GUNR];
             uint64_t bal[GUNR];
 #pragma unroll
             for (int u = 0; u < GUNR; ++u) {
-                const int f = f0 + u * 256 + (int)threadIdx.x;
+                const int f = f0 + u * kTauT + (int)threadIdx.x;
                 const int ff = f < T ? f : T - 1;          // past the end: the last entry (ignored); keeps sidx monotone
                 while (loff[sidx + 1] <= ff) ++sidx;
                 e[u] = lists[(size_t)sidx * lcap + (ff - loff[sidx])];
             }
 #pragma unroll
             for (int u = 0; u < GUNR; ++u) {
-                bal[u] = __ballot(f0 + u * 256 + (int)threadIdx.x < T && e[u].x > lo);
-                if (ln == 0) gbase[u * 4 + wv] = __popcll(bal[u]);
+                bal[u] = __ballot(f0 + u * kTauT + (int)threadIdx.x < T && e[u].x > lo);
+                if (ln == 0) gbase[u * kTauW + wv] = __popcll(bal[u]);
             }
             __syncthreads();
             if (wv == 0) {                                 // exclusive scan in (u, wave) order
                 const int c = gbase[ln];
                 const int inc = wave_incl_scan(c);
                 gbase[ln] = inc - c;
-                if (ln == 63) gbase[GUNR * 4] = inc;
+                if (ln == 63) gbase[GUNR * kTauW] = inc;
             }
             __syncthreads();
-            const int tot = gbase[GUNR * 4];
+            const int tot = gbase[GUNR * kTauW];
             if (total + tot <= kCandCap) {                 // block-uniform
 #pragma unroll
                 for (int u = 0; u < GUNR; ++u) {
                     if ((bal[u] >> ln) & 1u) {
-                        const int pos = total + gbase[u * 4 + wv] + lanes_below(bal[u]);
+                        const int pos = total + gbase[u * kTauW + wv] + lanes_below(bal[u]);
                         cand[pos] = e[u].x;
                         cslot[pos] = e[u].y;
                     }
@@ -915,7 +920,7 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
         r[3] = INFINITY;
         r[4] = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
+        for (int w2 = 0; w2 < kTauW; ++w2) {
             r[0] += red5[p5][w2][0];
             r[1] += red5[p5][w2][1];
             r[2] += red5[p5][w2][2];
@@ -927,7 +932,7 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
     // Every candidate x > lo, from LDS or from the lists.
     auto each_cand = [&](auto&& fn) {
         if (in_lds) {
-            for (int i = threadIdx.x; i < total; i += 256) fn(cand[i]);
+            for (int i = threadIdx.x; i < total; i += kTauT) fn(cand[i]);
         } else {
             each_flat([&](float2 e) {
                 if (e.x > lo) fn(e.x);
@@ -936,7 +941,54 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
     };
 
     float tau = lo;
-    if (beta >= 1.0f) {
+    if (beta >= 1.0f && in_lds && total <= kTauWaveCands) {
+        // Few candidates: one wave iterates over them in LDS with wave-level
+        // sums, so a step costs no block barrier (about 2 us of barrier
+        // latency per step otherwise, whatever the candidate count); the
+        // other waves wait at the barrier below.  Many candidates: the block
+        // shares them (a single wave's serial LDS reads would cost more).
+        __shared__ float sh_tau;
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            TauIter st = tau_iter_start(lo, xmax, tau_hint ? tau_hint[oh] : NAN, false);
+            for (int it = 0; it < 100 && !st.done; ++it) {   // wave-uniform state
+                const float t = st.t;
+                float s1 = 0.0f, s0 = 0.0f, kk = 0.0f, mn = INFINITY, rest = -INFINITY;
+                for (int i0 = 0; i0 < total; i0 += 4 * 64) {
+                    float xs[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = i0 + u * 64 + lane;
+                        xs[u] = i < total ? cand[i] : -INFINITY;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float x = xs[u];
+                        const float d = x - t;
+                        if (d > 0.0f) {
+                            s1 += powb(d, mode, beta);
+                            s0 += mode == kModeBeta1 ? 1.0f : (mode == kModeBeta2 ? d : powf(d, beta - 1.0f));
+                            kk += 1.0f;
+                            mn = fminf(mn, x);
+                        } else {
+                            rest = fmaxf(rest, x);
+                        }
+                    }
+                }
+                s1 = wave_sum(s1);
+                s0 = wave_sum(s0);
+                kk = wave_sum(kk);
+                mn = -wave_max(-mn);
+                rest = wave_max(rest);
+                if (mode == kModeBeta1) tau_iter_step<kModeBeta1>(st, lo, beta, s1, s0, kk, mn, rest);
+                else if (mode == kModeBeta2) tau_iter_step<kModeBeta2>(st, lo, beta, s1, s0, kk, mn, rest);
+                else tau_iter_step<kModeGeneral>(st, lo, beta, s1, s0, kk, mn, rest);
+            }
+            if (lane == 0) sh_tau = st.done ? st.tau : st.t;
+        }
+        __syncthreads();
+        tau = sh_tau;
+    } else if (beta >= 1.0f) {
         TauIter st = tau_iter_start(lo, xmax, tau_hint ? tau_hint[oh] : NAN, false);
         for (int it = 0; it < 100 && !st.done; ++it) {   // block-uniform state
             const float t = st.t;
@@ -982,7 +1034,7 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
     // from LDS, or from the lists when the candidates did not fit.
     auto each_cand2 = [&](auto&& fn) {
         if (in_lds) {
-            for (int i = threadIdx.x; i < total; i += 256) fn(make_float2(cand[i], cslot[i]));
+            for (int i = threadIdx.x; i < total; i += kTauT) fn(make_float2(cand[i], cslot[i]));
         } else {
             each_flat([&](float2 e) {
                 if (e.x > lo) fn(e);
@@ -1001,14 +1053,14 @@ static __global__ __launch_bounds__(256) void stream_tau_kernel(
         }
     });
     int soff, soff2, stotal, st2;
-    block_excl_scan2<4>(ns, 0, soff, soff2, &stotal, &st2, wsum);
+    block_excl_scan2<kTauW>(ns, 0, soff, soff2, &stotal, &st2, wsum);
     float2* sl_out = sup_list + oh * (size_t)nslot;
     each_cand2([&](float2 e) {
         if (e.x > tau) sl_out[soff++] = make_float2(powb(e.x - tau, mode, beta), e.y);
     });
     if (want_ref) {
-        kept = block_sum<4>(kept, red, phase);
-        nref = block_sum<4>(nref, red, phase);
+        kept = block_sum<kTauW>(kept, red, phase);
+        nref = block_sum<kTauW>(nref, red, phase);
     }
     if (threadIdx.x == 0) {
         tau_out[oh] = tau;
@@ -1816,11 +1868,15 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        stream_tau_kernel<<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(cands, ccount, cmax, pl.nsplit_s * lps,
-                                                              pl.cpb_s * kStreamSlots / lps, d.HQ, pl.nslot, mode,
-                                                              beta,
-                                                              io.tau_hint, io.tau_ref, io.tau, io.support, io.delta,
-                                                              io.supref, sup, supcnt);
+#define EKV_STREAM_TAU(M)                                                                                        \
+    stream_tau_kernel<M><<<dim3(d.HQ, d.B), dim3(kTauT), 0, s>>>(cands, ccount, cmax, pl.nsplit_s * lps,           \
+                                                                 pl.cpb_s * kStreamSlots / lps, d.HQ, pl.nslot,  \
+                                                                 beta, io.tau_hint, io.tau_ref, io.tau,          \
+                                                                 io.support, io.delta, io.supref, sup, supcnt)
+        if (mode == kModeBeta1) EKV_STREAM_TAU(kModeBeta1);
+        else if (mode == kModeBeta2) EKV_STREAM_TAU(kModeBeta2);
+        else EKV_STREAM_TAU(kModeGeneral);
+#undef EKV_STREAM_TAU
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         support_pv_kernel<T, D, R><<<dim3(kSupSplit, d.HQ, d.B), dim3(256), 0, s>>>(
