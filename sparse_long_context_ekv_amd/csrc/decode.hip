@@ -1,6 +1,8 @@
 // Sparse alpha-entmax decode: the workspace plan and the dispatch to the
 // per-dtype kernel launches (decode_bf16.hip, decode_f32.hip); the kernels
 // and what they compute are described in decode_kernels.h.
+#include <algorithm>
+
 #include "decode_kernels.h"
 
 namespace ekv {
@@ -32,11 +34,20 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         // Chunks per block: about kStreamBlocks blocks in all, at most
         // kStreamMaxChunks chunks per block; each block keeps up to 4 lists
         // per head (one per wave on bf16 keys), kStreamMaxLists per (b, h).
+        // The work is estimated from the pages the cache holds where that is
+        // less than B * max pages (sequences shorter than the table's width):
+        // about kStreamBlocks working blocks either way.  Where it is less
+        // than 3/4 of it (a ragged batch, most likely), blocks are capped at
+        // 16 chunks, so that the longest-first order can balance the CUs.
         const long nchunk = maxp > 0 ? (maxp + kStreamPpb - 1) / kStreamPpb : 1;
         const long units = (long)d.B * d.G;
-        long cpb = (nchunk * units + kStreamBlocks - 1) / kStreamBlocks;
+        const long cap_pages = (long)d.B * maxp;
+        const long work_pages = sparse ? cap_pages : std::min<long>(cap_pages, d.NP);
+        const long work_chunks = std::max<long>((work_pages + kStreamPpb - 1) / kStreamPpb, 1) * d.G;
+        long cpb = (work_chunks + kStreamBlocks - 1) / kStreamBlocks;
         if (cpb < 1) cpb = 1;
         if (cpb > kStreamMaxChunks) cpb = kStreamMaxChunks;
+        if (4 * work_pages < 3 * cap_pages && cpb > kStreamRaggedChunks) cpb = kStreamRaggedChunks;
         pl.cpb_s = (int)cpb;
         pl.nsplit_s = (int)((nchunk + cpb - 1) / cpb);
         // rows past kStreamMaxLists / 4 * kStreamMaxChunks chunks (16M tokens) are not built
@@ -48,7 +59,8 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         pl.off_sup = pl.off_cmax + align256(rows * sizeof(float));
         pl.off_supcnt = pl.off_sup + align256(bh * pl.nslot * sizeof(float2));
         pl.off_part3 = pl.off_supcnt + align256(bh * sizeof(int32_t));
-        pl.bytes = pl.off_part3 + align256(bh * kSupSplit * d.D * sizeof(float));
+        pl.off_order = pl.off_part3 + align256(bh * kSupSplit * d.D * sizeof(float));   // sequences by length
+        pl.bytes = pl.off_order + align256((size_t)d.B * sizeof(int32_t));
     } else {
         // softmax: logits, chunk partials (max, sum exp, count), PV partials
         pl.spb = sparse ? 256 : 4096;

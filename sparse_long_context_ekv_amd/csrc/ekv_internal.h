@@ -65,7 +65,7 @@ struct DecodePlan {
     int nsplit_s;    // candidate-stream blocks per (b, g)
     int too_long;    // rows longer than the stream path is built for
     size_t off_logits, off_part1, off_part3;
-    size_t off_cands, off_ccount, off_cmax, off_sup, off_supcnt;
+    size_t off_cands, off_ccount, off_cmax, off_sup, off_supcnt, off_order;
     size_t bytes;
 };
 DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha);
