@@ -495,9 +495,31 @@ constexpr int kSupSplit = 8;                          // PV blocks per head over
 constexpr int kStreamUnroll = 8;                      // pages' tiles in flight per row while streaming
 
 // The batch's sequences by length, longest first (ties: lower index first):
-// order[rank] = b.  One block; rank_b counts the sequences that go before b
-// (B^2 / 1024 steps per thread, so batches past kOrderMaxB keep their order).
+// order[rank] = b, where rank_b counts the sequences that go before b.
+// Batches of at most kOrderLdsB sequences: every candidate-stream block
+// computes the order itself into LDS (B^2 / 256 steps per thread);
+// larger ones: this one-block kernel, once (B^2 / 1024 steps per thread, so
+// batches past kOrderMaxB keep their order).
+constexpr int kOrderLdsB = 256;
 constexpr int kOrderMaxB = 4096;
+
+// The b of rank `rank`: from `order` (device, larger batches) or computed
+// into `sh` by the block (ends with a barrier).
+__device__ __forceinline__ int stream_seq(const int32_t* __restrict__ seq_lens, int B, int MP,
+                                          const int32_t* __restrict__ order, int rank, int* sh) {
+    if (B > kOrderLdsB) return order[rank];
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int nb = seq_len_at(seq_lens, b, MP);
+        int r = 0;
+        for (int c = 0; c < B; ++c) {
+            const int nc = seq_len_at(seq_lens, c, MP);
+            r += (nc > nb || (nc == nb && c < b)) ? 1 : 0;
+        }
+        sh[r] = b;
+    }
+    __syncthreads();
+    return sh[rank];
+}
 static __global__ __launch_bounds__(1024) void order_by_length_kernel(const int32_t* __restrict__ seq_lens, int B,
                                                                       int MP, int32_t* __restrict__ order) {
     if (B > kOrderMaxB) {
@@ -519,7 +541,7 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void cand_stream_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int cpb, int nsplit,
+    const int32_t* __restrict__ sel_count, int sel_stride, int B, int G, int MP, int NP, int cpb, int nsplit,
     const int32_t* __restrict__ order, float inv_sqrt_d, float a, float2* __restrict__ cands,
     int32_t* __restrict__ ccount, float* __restrict__ cmax) {
     constexpr int CH = D / kRow;
@@ -532,8 +554,9 @@ __global__ __launch_bounds__(256) void cand_stream_kernel(
     // G tiles of a physical page are adjacent in the cache); sequences
     // longest first (`order`), so that on a ragged batch the long sequences'
     // blocks start first and the short ones fill in behind them.
+    __shared__ int sh_order[kOrderLdsB];
     const int g = blockIdx.x % G, rest = blockIdx.x / G;
-    const int split = rest % nsplit, b = order[rest / nsplit];
+    const int split = rest % nsplit, b = stream_seq(seq_lens, B, MP, order, rest / nsplit, sh_order);
     const int unit = b * G + g;
     const int HQ = G * R;
     const int n = seq_len_at(seq_lens, b, MP);
@@ -634,7 +657,7 @@ template <int D, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cand_stream_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_pages,
-    const int32_t* __restrict__ sel_count, int sel_stride, int G, int MP, int NP, int cpb, int nsplit,
+    const int32_t* __restrict__ sel_count, int sel_stride, int B, int G, int MP, int NP, int cpb, int nsplit,
     const int32_t* __restrict__ order, float inv_sqrt_d, float a, float2* __restrict__ cands,
     int32_t* __restrict__ ccount, float* __restrict__ cmax) {
     constexpr int KPW = R <= 4 ? 8 : 4;                  // pages per wave per step (32 or 16 KiB in flight)
@@ -648,8 +671,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     __shared__ int sh_lp[kStreamMaxChunks * kStreamPpb], sh_phys[kStreamMaxChunks * kStreamPpb];
     // Block order: group fastest, then split, then sequence, longest first
     // (see cand_stream_kernel).
+    __shared__ int sh_order[kOrderLdsB];
     const int g = blockIdx.x % G, rest = blockIdx.x / G;
-    const int split = rest % nsplit, b = order[rest / nsplit];
+    const int split = rest % nsplit, b = stream_seq(seq_lens, B, MP, order, rest / nsplit, sh_order);
     const int unit = b * G + g;
     const int HQ = G * R;
     const int n = seq_len_at(seq_lens, b, MP);
@@ -1882,20 +1906,22 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         float2* sup = (float2*)(ws + pl.off_sup);
         int32_t* supcnt = (int32_t*)(ws + pl.off_supcnt);
         int32_t* order = (int32_t*)(ws + pl.off_order);
-        order_by_length_kernel<<<dim3(1), dim3(1024), 0, s>>>(sl, d.B, d.MP, order);
-        hipError_t e0 = hipGetLastError();
-        if (e0 != hipSuccess) return e0;
+        if (d.B > kOrderLdsB) {
+            order_by_length_kernel<<<dim3(1), dim3(1024), 0, s>>>(sl, d.B, d.MP, order);
+            hipError_t e0 = hipGetLastError();
+            if (e0 != hipSuccess) return e0;
+        }
         // lists per split: one per wave on bf16 keys, one per block otherwise
         int lps = 1;
         if constexpr (std::is_same<T, bf16_t>::value) {
             lps = 4;
             cand_stream_mfma_kernel<D, R><<<dim3(pl.nsplit_s * units), dim3(256), 0, s>>>(
-                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP, pl.cpb_s,
-                pl.nsplit_s, order, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.B, d.G, d.MP, d.NP,
+                pl.cpb_s, pl.nsplit_s, order, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
         } else {
             cand_stream_kernel<T, D, R><<<dim3(pl.nsplit_s * units), dim3(256), 0, s>>>(
-                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP, pl.cpb_s,
-                pl.nsplit_s, order, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
+                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.B, d.G, d.MP, d.NP,
+                pl.cpb_s, pl.nsplit_s, order, 1.0f / sqrtf((float)D), alpha - 1.0f, cands, ccount, cmax);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -541,6 +541,29 @@ def test_empty_sequence_and_short_sequence():
     assert np.abs(H.to_np(dec.buf.out[0]) - ref["out"]).max() <= H.OUT_ATOL
 
 
+def test_full_cache_many_sequences():
+    """Full-cache decode of a batch of 300 ragged sequences (past the 256
+    that the streamed path orders by length inside each block: the one-block
+    ordering kernel runs), with empty and one-token sequences among them;
+    sampled sequences against the oracle."""
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(1, 700, size=300)]
+    lens[3], lens[100], lens[299] = 0, 1, 2500
+    cfg = W.CONFIGS[2].scaled(batch=300)
+    wl = W.make_workload(cfg, "cuda", seq_lens=lens)
+    c = wl.cfg
+    out, tau, sup, _, _ = _run_decode(wl, 1.5)
+    for b in (0, 3, 100, 157, 298, 299):
+        q, K, V, n = H.seq_logical(wl, b)
+        if n == 0:
+            assert bool((out[b] == 0).all()) and bool((tau[b] == -float("inf")).all())
+            continue
+        ref = oracle.decode.decode(q, K, V, None, 1.5)
+        assert np.abs(H.to_np(out[b]) - ref["out"]).max() <= H.OUT_ATOL
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau[b, h]), ref["tau"][h])
+
+
 @pytest.mark.parametrize("name,alpha", [("llama-ragged", 1.5), ("llama-ragged", 2.0), ("long-with-empty", 1.5)])
 def test_full_cache_bitwise_reproducible(name, alpha):
     """The streamed full-cache path shares its running max between a block's
