@@ -485,7 +485,7 @@ constexpr int kStreamPpb = 32;                        // pages per chunk
 constexpr int kStreamSlots = kStreamPpb * kPage;      // 512 slots per chunk
 constexpr int kStreamMaxChunks = 64;                  // chunks per candidate-stream block at most
 constexpr int kStreamMaxLists = 2048;                 // candidate lists per (b, h) at most (4 per block)
-constexpr int kStreamStage = 1024;                    // candidates staged in LDS per wave (bf16 stream)
+constexpr int kStreamStage = 1536;                    // candidates staged in LDS per wave (bf16 stream; 65 KiB per block)
 constexpr int kTauT = 512;                            // threads of the streamed threshold kernel (2 blocks per CU)
 constexpr int kTauWaveCands = 2048;                   // at most this many candidates: one wave iterates
 constexpr int kTauW = kTauT / 64;
