@@ -230,6 +230,8 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  *   of [EKV] section 3.1 and Appendix E.1.
  * An empty candidate set (seq_lens[b] == 0 or sel_count == 0) gives
  *   out = 0, tau = -inf, support = 0, delta = 1, support_ref = 0.
+ * Rows of more than 2^20 pages (16M tokens: max_pages_per_seq for
+ *   sel_pages == NULL, else sel_stride) return EKV_ERR_UNSUPPORTED.
  * Needs a workspace (see conventions); its size depends on sel_pages being
  * NULL or not and on sel_stride.                                           */
 ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,

@@ -48,6 +48,9 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         if (cpb < 1) cpb = 1;
         if (cpb > kStreamMaxChunks) cpb = kStreamMaxChunks;
         if (4 * work_pages < 3 * cap_pages && cpb > kStreamRaggedChunks) cpb = kStreamRaggedChunks;
+        // never fewer chunks per block than the longest row needs to fit its lists
+        const long cpb_need = (nchunk + kStreamMaxLists / 4 - 1) / (kStreamMaxLists / 4);
+        if (cpb < cpb_need) cpb = std::min<long>(cpb_need, kStreamMaxChunks);
         pl.cpb_s = (int)cpb;
         pl.nsplit_s = (int)((nchunk + cpb - 1) / cpb);
         // rows past kStreamMaxLists / 4 * kStreamMaxChunks chunks (16M tokens) are not built
