@@ -505,6 +505,37 @@ def test_sparse_decode_on_oracle_selection(name, alpha):
             assert int(supref[b, h]) <= int(sup_full[b, h]) + _support_slack(full["s"][h], full["tau"][h], alpha)
 
 
+@pytest.mark.parametrize("heads,groups,dim,alpha", [(8, 8, 128, 1.5), (16, 8, 64, 1.5), (64, 8, 128, 1.5),
+                                                    (32, 8, 64, 2.0), (12, 6, 128, 4.0 / 3.0), (8, 1, 64, 1.5)])
+def test_decode_shapes_bf16(heads, groups, dim, alpha):
+    """bf16 keys at every r (1, 2, 4, 8) and d = 64: the matrix-core logits
+    of the fused path (on the oracle's top-k selection) and the matrix-core
+    candidate stream of the full-cache path, against the oracle; a ragged
+    batch with a sequence ending inside a page."""
+    cfg = W.CONFIGS[3].scaled(batch=3, num_q_heads=heads, num_kv_groups=groups, head_dim=dim)
+    wl = W.make_workload(cfg, "cuda", seq_lens=[1499, 37, 2900])
+    c = wl.cfg
+    budget = 48
+    sels = []
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sels.append(oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", alpha, budget)["sel"])
+    sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, budget)
+    out_s, tau_s, sup_s, _, _ = _run_decode(wl, alpha, sel, cnt, budget)
+    out_f, tau_f, sup_f, _, _ = _run_decode(wl, alpha)
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, sels[b], alpha)
+        full = oracle.decode.decode(q, K, V, None, alpha)
+        assert np.abs(H.to_np(out_s[b]) - sp["out"]).max() <= H.OUT_ATOL, b
+        assert np.abs(H.to_np(out_f[b]) - full["out"]).max() <= H.OUT_ATOL, b
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau_s[b, h]), sp["tau"][h]), (b, h)
+            assert H.tau_close(float(tau_f[b, h]), full["tau"][h]), (b, h)
+            assert abs(int(sup_f[b, h]) - int(full["support"][h])) <= _support_slack(full["s"][h], full["tau"][h],
+                                                                                      alpha)
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama-ragged"])
 def test_pipeline_end_to_end(name):
     wl = workload(name)
