@@ -24,13 +24,9 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     pl.ppb = 1 << pl.lg_ppb;
     pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
     if (pl.nchunk1 < 1) pl.nchunk1 = 1;
-    if (pl.fused) {
-        // selected logits [B][HQ][nslot]
-        pl.off_logits = 0;
-        pl.bytes = align256(bh * pl.nslot * sizeof(float));
-    } else if (pl.stream) {
-        // per (b, h, chunk): candidate list (x, slot), count, max; per (b, h):
-        // support list (p, slot), its count, kSupSplit partial outputs
+    // one-pass softmax for bf16 keys (alpha = 1): the streamed path's block split
+    pl.smx1 = !(alpha > 1.0f) && d.kv_bf16;
+    if (pl.stream || pl.smx1) {
         // Chunks per block: about kStreamBlocks blocks in all, at most
         // kStreamMaxChunks chunks per block; each block keeps up to 4 lists
         // per head (one per wave on bf16 keys), kStreamMaxLists per (b, h).
@@ -40,7 +36,6 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         // than 3/4 of it (a ragged batch, most likely), blocks are capped at
         // 16 chunks, so that the longest-first order can balance the CUs.
         const long nchunk = maxp > 0 ? (maxp + kStreamPpb - 1) / kStreamPpb : 1;
-        const long units = (long)d.B * d.G;
         const long cap_pages = (long)d.B * maxp;
         const long work_pages = sparse ? cap_pages : std::min<long>(cap_pages, d.NP);
         const long work_chunks = std::max<long>((work_pages + kStreamPpb - 1) / kStreamPpb, 1) * d.G;
@@ -55,6 +50,14 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         pl.nsplit_s = (int)((nchunk + cpb - 1) / cpb);
         // rows past kStreamMaxLists / 4 * kStreamMaxChunks chunks (16M tokens) are not built
         pl.too_long = 4L * pl.nsplit_s > kStreamMaxLists;
+    }
+    if (pl.fused) {
+        // selected logits [B][HQ][nslot]
+        pl.off_logits = 0;
+        pl.bytes = align256(bh * pl.nslot * sizeof(float));
+    } else if (pl.stream) {
+        // per (b, h, split, wave): candidate list (x, slot), count, max; per
+        // (b, h): support list (p, slot), its count, kSupSplit partial outputs
         const size_t rows = bh * pl.nsplit_s * 4;              // list counts and maxima
         pl.off_cands = 0;
         pl.off_ccount = pl.off_cands + align256(bh * pl.nsplit_s * pl.cpb_s * kStreamSlots * sizeof(float2));
@@ -63,6 +66,11 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         pl.off_supcnt = pl.off_sup + align256(bh * pl.nslot * sizeof(float2));
         pl.off_part3 = pl.off_supcnt + align256(bh * sizeof(int32_t));
         pl.off_order = pl.off_part3 + align256(bh * kSupSplit * d.D * sizeof(float));   // sequences by length
+        pl.bytes = pl.off_order + align256((size_t)d.B * sizeof(int32_t));
+    } else if (pl.smx1) {
+        // per (b, h, split): o [D], running max, sum of exp, valid count
+        pl.off_part3 = 0;
+        pl.off_order = align256(bh * pl.nsplit_s * (d.D + 4) * sizeof(float));
         pl.bytes = pl.off_order + align256((size_t)d.B * sizeof(int32_t));
     } else {
         // softmax: logits, chunk partials (max, sum exp, count), PV partials

@@ -822,6 +822,226 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
 }
 
+// --------------------------------------------- one-pass softmax (bf16) ----
+// alpha = 1 over bf16 keys (full cache or a selection): keys and values are
+// read once.  The streamed path's blocks (ranges of one (b, g), longest
+// sequences first); every wave takes its own pages, 4 per step: logits on
+// the matrix cores, then per head a running max m, a running sum
+// l = sum exp(s - m) and o = sum exp(s - m) v over the wave's tokens, both
+// rescaled by exp(m_old - m_new) when m grows (the max-shifted sums of the
+// log-partition, so nothing overflows).  The next step's K tiles are read
+// before this step's softmax arithmetic, its V tiles after this step's PV.
+// Lane l owns value channels [D/64 l, D/64 (l + 1)) of every token; a
+// token's weight comes from the lane that holds its logit (v_readlane).
+// The block's four waves combine (m, l, o) by rescaling to the larger max;
+// softmax_merge_kernel combines the blocks of a row the same way:
+// out = o / l, tau = m + log l.
+template <int D, int KPW>
+struct VRows {
+    static constexpr int VC = D / 64;                 // channels per lane
+    uint32_t w[KPW][kPage];                           // VC bf16 of each token (low half when VC = 1)
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ v_cache, const int* sh_phys, int i, int i0,
+                                         int i1, int G, int g) {
+        const int l = threadIdx.x & 63;
+#pragma unroll
+        for (int u = 0; u < KPW; ++u) {
+            const int ii = i + 4 * u;
+            const int t = ii < i1 ? ii - i0 : 0;
+            const int ph = sh_phys[t];
+            const bf16_t* src = v_cache + ((size_t)(ii < i1 && ph >= 0 ? ph : 0) * G + g) * kPage * D + VC * l;
+#pragma unroll
+            for (int tk = 0; tk < kPage; ++tk) {
+                if constexpr (VC == 2) w[u][tk] = *reinterpret_cast<const uint32_t*>(src + (size_t)tk * D);
+                else w[u][tk] = (uint32_t)src[(size_t)tk * D];
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int u, int tk, int c) const {
+        return c == 0 ? __uint_as_float(w[u][tk] << 16) : __uint_as_float(w[u][tk] & 0xffff0000u);
+    }
+};
+
+template <int D, int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void softmax_stream_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache, const bf16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel_pages, const int32_t* __restrict__ sel_count, int sel_stride, int B, int G,
+    int MP, int NP, int cpb, int nsplit, const int32_t* __restrict__ order, float inv_sqrt_d,
+    float* __restrict__ part) {
+    constexpr int KPW = R <= 4 ? 4 : 2;                  // pages per wave per step
+    constexpr int SP = 4 * KPW;
+    constexpr int VC = D / 64;
+    __shared__ int sh_order[kOrderLdsB];
+    __shared__ int sh_lp[kStreamMaxChunks * kStreamPpb], sh_phys[kStreamMaxChunks * kStreamPpb];
+    __shared__ float wm[4][R], wl[4][R], wc[4];
+    __shared__ float wo[4][R][D];
+    // block order as in the candidate stream: group fastest, then split, then
+    // sequence, longest first
+    const int g = blockIdx.x % G, rest = blockIdx.x / G;
+    const int split = rest % nsplit, b = stream_seq(seq_lens, B, MP, order, rest / nsplit, sh_order);
+    const int unit = b * G + g;
+    const int HQ = G * R;
+    const int n = seq_len_at(seq_lens, b, MP);
+    const int M = num_pages(n);
+    const int cnt = sel_pages ? min(max(sel_count[unit], 0), sel_stride) : M;
+    const int span = cpb * kStreamPpb;
+    const int p0 = split * span;
+    const int p1 = span <= kStreamMaxChunks * kStreamPpb ? min(cnt, p0 + span) : p0;   // else: an empty range
+    const int32_t* sel = sel_pages ? sel_pages + (size_t)unit * sel_stride : nullptr;
+    for (int t = threadIdx.x; t < min(span, kStreamMaxChunks * kStreamPpb); t += blockDim.x) {
+        const int ii = p0 + t;
+        const int lp = ii < p1 ? (sel ? sel[ii] : ii) : -1;
+        const int phys = (lp >= 0 && lp < M) ? page_table[(size_t)b * MP + lp] : -1;
+        const bool ok = phys >= 0 && phys < NP;
+        sh_lp[t] = ok ? lp : -1;
+        sh_phys[t] = ok ? phys : -1;
+    }
+    __syncthreads();
+
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, tq = l & 15, hq = l >> 4;
+    float m[R], ls[R], o[R][VC];
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+        m[h] = -INFINITY;
+        ls[h] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < VC; ++c) o[h][c] = 0.0f;
+    }
+    float valid = 0.0f;
+    MfmaQ<D, R> mq;
+    mq.load(q + ((size_t)b * HQ + g * R) * D);
+    MfmaKPages<D, KPW> kp;
+    VRows<D, KPW> vr;
+    if (p0 < p1) {
+        kp.load(k_cache, sh_lp, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g);
+        vr.load(v_cache, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g);
+    }
+    for (int i0 = p0; i0 < p1; i0 += SP) {                  // block-uniform
+        const int i1 = min(p1, i0 + SP);
+        f32x4_t acc[KPW];
+        kp.template contract<R>(mq, acc);
+        float sv[KPW][4];
+#pragma unroll
+        for (int u = 0; u < KPW; ++u) {
+            const bool live = i0 + wv + 4 * u < i1 && kp.ok[u] && kp.lp[u] * kPage + tq < n;
+            valid += (float)__popcll(__ballot(live) & 0xffffull);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[u][j] = live ? acc[u][j] * inv_sqrt_d : -INFINITY;
+        }
+        // the next step's key tiles go out before this step's arithmetic
+        if (i1 < p1) kp.load(k_cache, sh_lp + (i1 - p0), sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
+        // new running maxima (uniform per head) and the rescaling of l and o
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+            const int jr = h & 3, rw = 16 * (h >> 2);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < KPW; ++u) mx = fmaxf(mx, sv[u][jr]);
+            const float mstep = readlane(row_max16(mx), rw);
+            const float mnew = fmaxf(m[h], mstep);
+            const float sc = m[h] > -INFINITY ? expf(m[h] - mnew) : 0.0f;
+            m[h] = mnew;
+            ls[h] *= sc;
+#pragma unroll
+            for (int c = 0; c < VC; ++c) o[h][c] *= sc;
+        }
+        // weights exp(s - m) in the lanes that hold the logits
+        float pw[KPW][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mh = (R <= 4 || hq == 0) ? m[j < R ? j : 0] : m[(4 + j) < R ? 4 + j : 0];
+            float rs = 0.0f;
+#pragma unroll
+            for (int u = 0; u < KPW; ++u) {
+                pw[u][j] = sv[u][j] > -INFINITY ? expf(sv[u][j] - mh) : 0.0f;
+                rs += pw[u][j];
+            }
+            rs = row_sum16(rs);
+#pragma unroll
+            for (int h = j; h < R; h += 4) ls[h] += readlane(rs, 16 * (h >> 2));
+        }
+        // PV: every token's weight from its lane, this lane's value channels
+#pragma unroll
+        for (int u = 0; u < KPW; ++u) {
+#pragma unroll
+            for (int tk = 0; tk < kPage; ++tk) {
+#pragma unroll
+                for (int h = 0; h < R; ++h) {
+                    const float w = readlane(pw[u][h & 3], 16 * (h >> 2) + tk);
+#pragma unroll
+                    for (int c = 0; c < VC; ++c) o[h][c] = fmaf(w, vr.get(u, tk, c), o[h][c]);
+                }
+            }
+        }
+        // the next step's value tiles
+        if (i1 < p1) vr.load(v_cache, sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
+    }
+    // the block's four waves -> one (m, l, o, count) per head
+    if (l == 0) {
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+            wm[wv][h] = m[h];
+            wl[wv][h] = ls[h];
+        }
+        wc[wv] = valid;
+    }
+#pragma unroll
+    for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int c = 0; c < VC; ++c) wo[wv][h][VC * l + c] = o[h][c];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
+        const int h = idx / D, c = idx - h * D;
+        float mm = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) mm = fmaxf(mm, wm[w2][h]);
+        float oo = 0.0f, ll = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const float e = wm[w2][h] > -INFINITY ? expf(wm[w2][h] - mm) : 0.0f;
+            oo += wo[w2][h][c] * e;
+            ll += wl[w2][h] * e;
+        }
+        float* dst = part + (((size_t)b * HQ + g * R + h) * nsplit + split) * (D + 4);
+        dst[c] = oo;
+        if (c == 0) {
+            dst[D] = mm;
+            dst[D + 1] = ll;
+            dst[D + 2] = ((wc[0] + wc[1]) + wc[2]) + wc[3];
+        }
+    }
+}
+
+// The row's blocks, combined: weights exp(m_s - max m) in block order.
+template <int D>
+static __global__ __launch_bounds__(D) void softmax_merge_kernel(
+    const float* __restrict__ part, int HQ, int nsplit, const float* __restrict__ tau_ref,
+    float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
+    float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
+    const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+    const size_t oh = (size_t)b * HQ + h;
+    const float* pr = part + oh * nsplit * (D + 4);
+    float mm = -INFINITY;
+    for (int s2 = 0; s2 < nsplit; ++s2) mm = fmaxf(mm, pr[(size_t)s2 * (D + 4) + D]);
+    float oo = 0.0f, ll = 0.0f, cc = 0.0f;
+    for (int s2 = 0; s2 < nsplit; ++s2) {
+        const float* e = pr + (size_t)s2 * (D + 4);
+        const float w = e[D] > -INFINITY ? expf(e[D] - mm) : 0.0f;
+        oo += e[c] * w;
+        ll += e[D + 1] * w;
+        cc += e[D + 2];
+    }
+    const bool any = cc > 0.0f;
+    out[oh * D + c] = any ? oo / ll : 0.0f;
+    if (c == 0) {
+        tau_out[oh] = any ? mm + logf(ll) : -INFINITY;
+        if (support_out) support_out[oh] = (int32_t)cc;
+        const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+        if (delta_out) delta_out[oh] = any ? 1.0f - ll * expf(mm - tref) : 1.0f;
+        if (supref_out) supref_out[oh] = (int32_t)cc;   // softmax: every token has p > 0
+    }
+}
+
 template <int MODE>
 static __global__ __launch_bounds__(kTauT) void stream_tau_kernel(
     const float2* __restrict__ cands, const int32_t* __restrict__ ccount, const float* __restrict__ cmax,
@@ -1942,6 +2162,26 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
         if (e != hipSuccess) return e;
         reduce_kernel<<<dim3(d.HQ, d.B), dim3(kReduceThreads), 0, s>>>(part3, d.HQ, D, kSupSplit, io.out);
         return hipGetLastError();
+    }
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (pl.smx1) {
+            float* part = (float*)(ws + pl.off_part3);
+            int32_t* order = (int32_t*)(ws + pl.off_order);
+            if (d.B > kOrderLdsB) {
+                order_by_length_kernel<<<dim3(1), dim3(1024), 0, s>>>(sl, d.B, d.MP, order);
+                hipError_t e0 = hipGetLastError();
+                if (e0 != hipSuccess) return e0;
+            }
+            softmax_stream_kernel<D, R><<<dim3(pl.nsplit_s * units), dim3(256), 0, s>>>(
+                (const bf16_t*)q, (const bf16_t*)k_cache, (const bf16_t*)v_cache, pt, sl, sel_pages, sel_count,
+                sel_stride, d.B, d.G, d.MP, d.NP, pl.cpb_s, pl.nsplit_s, order, 1.0f / sqrtf((float)D), part);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            softmax_merge_kernel<D><<<dim3(d.HQ, d.B), dim3(D), 0, s>>>(part, d.HQ, pl.nsplit_s, io.tau_ref,
+                                                                       io.out, io.tau, io.support, io.delta,
+                                                                       io.supref);
+            return hipGetLastError();
+        }
     }
     // softmax: logits with chunk partials, log-partition, PV over every slot
     logits_kernel<T, D, R, true><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(

@@ -52,6 +52,7 @@ struct DecodePlan {
     int sparse;      // selection given
     int fused;       // sparse entmax within kFusedMaxSlots: logits kernel + one tau/PV kernel per (b, g)
     int stream;      // entmax otherwise: candidate stream, threshold, PV over the support
+    int smx1;        // softmax over bf16 keys: one pass (streamed blocks), then a merge
     int nslot;       // slots per (b, h): selected (or all) pages x page size
     // fused and softmax paths: logits kernel blocks
     int lg_ppb;      // log2 of ppb
