@@ -779,6 +779,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         bool live[KPW];
 #pragma unroll
         for (int u = 0; u < KPW; ++u) live[u] = i0 + wv + 4 * u < i1 && kp.ok[u] && kp.lp[u] * kPage + tq < n;
+        // the next step's reads go out as soon as this step's tiles are
+        // contracted (after any copy-out), before its candidates are taken
+        if (i1 < p1) kp.load(k_cache, sh_lp + (i1 - p0), sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
         float x[KPW][4];
         float lo[4];
 #pragma unroll
@@ -789,12 +792,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 x[u][j] = live[u] ? a * (acc[u][j] * inv_sqrt_d) : -INFINITY;
                 m = fmaxf(m, x[u][j]);
             }
-            rmax[j] = fmaxf(rmax[j], row_max16(m));          // the row's head 4 hq + j
-            if (4 * hq + j < R) rmax[j] = fmaxf(rmax[j], ord_unkey(atomicMax(&smax[4 * hq + j], ord_key(rmax[j]))));
+            rmax[j] = fmaxf(rmax[j], row_max16(m));          // the row's head 4 hq + j, in all 16 lanes
+        }
+        // the block's running max: the first lane of each row of heads
+        // publishes its row's maxima (one LDS round trip for all four) and the
+        // result goes back to the row's lanes
+        uint32_t got[4] = {0u, 0u, 0u, 0u};
+        if (tq == 0 && 4 * hq < R) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < R) got[j] = atomicMax(&smax[4 * hq + j], ord_key(rmax[j]));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < R) {
+                float gb = ord_unkey(got[j]);
+                gb = NR == 1 ? readlane(gb, 0) : (hq == 0 ? readlane(gb, 0) : readlane(gb, 16));
+                if (4 * hq + j < R) rmax[j] = fmaxf(rmax[j], gb);
+            }
             lo[j] = rmax[j] - 1.0f;                          // -inf: nothing valid yet
         }
-        // the next step's reads go out before this step's candidates are taken
-        if (i1 < p1) kp.load(k_cache, sh_lp + (i1 - p0), sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
 #pragma unroll
         for (int u = 0; u < KPW; ++u) {
             const float slot = __int_as_float((i0 + wv + 4 * u) * kPage + tq);
