@@ -506,12 +506,15 @@ def test_sparse_decode_on_oracle_selection(name, alpha):
 
 
 @pytest.mark.parametrize("heads,groups,dim,alpha", [(8, 8, 128, 1.5), (16, 8, 64, 1.5), (64, 8, 128, 1.5),
-                                                    (32, 8, 64, 2.0), (12, 6, 128, 4.0 / 3.0), (8, 1, 64, 1.5)])
+                                                    (32, 8, 64, 2.0), (12, 6, 128, 4.0 / 3.0), (8, 1, 64, 1.5),
+                                                    (8, 8, 128, 1.0), (16, 8, 64, 1.0), (64, 8, 128, 1.0),
+                                                    (32, 8, 128, 1.0)])
 def test_decode_shapes_bf16(heads, groups, dim, alpha):
     """bf16 keys at every r (1, 2, 4, 8) and d = 64: the matrix-core logits
     of the fused path (on the oracle's top-k selection) and the matrix-core
     candidate stream of the full-cache path, against the oracle; a ragged
-    batch with a sequence ending inside a page."""
+    batch with a sequence ending inside a page.  alpha = 1: the one-pass
+    softmax, over the selection and over the whole cache."""
     cfg = W.CONFIGS[3].scaled(batch=3, num_q_heads=heads, num_kv_groups=groups, head_dim=dim)
     wl = W.make_workload(cfg, "cuda", seq_lens=[1499, 37, 2900])
     c = wl.cfg
@@ -572,30 +575,32 @@ def test_empty_sequence_and_short_sequence():
     assert np.abs(H.to_np(dec.buf.out[0]) - ref["out"]).max() <= H.OUT_ATOL
 
 
-def test_full_cache_many_sequences():
+@pytest.mark.parametrize("alpha", [1.5, 1.0])
+def test_full_cache_many_sequences(alpha):
     """Full-cache decode of a batch of 300 ragged sequences (past the 256
     that the streamed path orders by length inside each block: the one-block
     ordering kernel runs), with empty and one-token sequences among them;
-    sampled sequences against the oracle."""
+    sampled sequences against the oracle (entmax and the one-pass softmax)."""
     rng = np.random.default_rng(11)
     lens = [int(x) for x in rng.integers(1, 700, size=300)]
     lens[3], lens[100], lens[299] = 0, 1, 2500
     cfg = W.CONFIGS[2].scaled(batch=300)
     wl = W.make_workload(cfg, "cuda", seq_lens=lens)
     c = wl.cfg
-    out, tau, sup, _, _ = _run_decode(wl, 1.5)
+    out, tau, sup, _, _ = _run_decode(wl, alpha)
     for b in (0, 3, 100, 157, 298, 299):
         q, K, V, n = H.seq_logical(wl, b)
         if n == 0:
             assert bool((out[b] == 0).all()) and bool((tau[b] == -float("inf")).all())
             continue
-        ref = oracle.decode.decode(q, K, V, None, 1.5)
+        ref = oracle.decode.decode(q, K, V, None, alpha)
         assert np.abs(H.to_np(out[b]) - ref["out"]).max() <= H.OUT_ATOL
         for h in range(c.num_q_heads):
             assert H.tau_close(float(tau[b, h]), ref["tau"][h])
 
 
-@pytest.mark.parametrize("name,alpha", [("llama-ragged", 1.5), ("llama-ragged", 2.0), ("long-with-empty", 1.5)])
+@pytest.mark.parametrize("name,alpha", [("llama-ragged", 1.5), ("llama-ragged", 2.0), ("long-with-empty", 1.5),
+                                        ("llama-ragged", 1.0)])
 def test_full_cache_bitwise_reproducible(name, alpha):
     """The streamed full-cache path shares its running max between a block's
     waves through an atomic, so the candidate lists may hold other extra
@@ -606,6 +611,37 @@ def test_full_cache_bitwise_reproducible(name, alpha):
         again = _run_decode(wl, alpha)
         for a, b in zip(first[:3], again[:3]):
             assert torch.equal(a, b)
+
+
+def test_softmax_large_logits():
+    """Softmax over logits in the hundreds (the query scaled by 40): every
+    block's sums are taken relative to its running max and the merge
+    rescales them, so nothing overflows; against the oracle, full cache
+    and over a selection."""
+    base = workload("llama-ragged")
+    wl = W.Workload(cfg=base.cfg, q=(base.q.float() * 40.0).to(base.q.dtype), k_cache=base.k_cache,
+                    v_cache=base.v_cache, page_table=base.page_table, seq_lens=base.seq_lens,
+                    seq_lens_host=base.seq_lens_host, max_pages=base.max_pages, num_phys=base.num_phys, planted={})
+    c = wl.cfg
+    budget = 40
+    sels = []
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sels.append(oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", 1.0, budget)["sel"])
+    sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, budget)
+    out_f, tau_f, sup_f, _, _ = _run_decode(wl, 1.0)
+    out_s, tau_s, _, _, _ = _run_decode(wl, 1.0, sel, cnt, budget)
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        full = oracle.decode.decode(q, K, V, None, 1.0)
+        assert float(np.abs(full["s"]).max()) > 100.0
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, sels[b], 1.0)
+        assert np.abs(H.to_np(out_f[b]) - full["out"]).max() <= H.OUT_ATOL, b
+        assert np.abs(H.to_np(out_s[b]) - sp["out"]).max() <= H.OUT_ATOL, b
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau_f[b, h]), full["tau"][h]), (b, h)
+            assert H.tau_close(float(tau_s[b, h]), sp["tau"][h]), (b, h)
+            assert int(sup_f[b, h]) == n
 
 
 def test_bitwise_reproducible():
