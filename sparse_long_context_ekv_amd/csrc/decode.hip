@@ -34,7 +34,7 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         // less than B * max pages (sequences shorter than the table's width):
         // about kStreamBlocks working blocks either way.  Where it is less
         // than 3/4 of it (a ragged batch, most likely), blocks are capped at
-        // 16 chunks, so that the longest-first order can balance the CUs.
+        // 24 chunks, so that the longest-first order can balance the CUs.
         const long nchunk = maxp > 0 ? (maxp + kStreamPpb - 1) / kStreamPpb : 1;
         const long cap_pages = (long)d.B * maxp;
         const long work_pages = sparse ? cap_pages : std::min<long>(cap_pages, d.NP);

@@ -490,7 +490,7 @@ constexpr int kTauT = 512;                            // threads of the streamed
 constexpr int kTauWaveCands = 2048;                   // at most this many candidates: one wave iterates
 constexpr int kTauW = kTauT / 64;
 constexpr int kStreamBlocks = 512;                    // aim: about this many candidate-stream blocks (2 per CU)
-constexpr int kStreamRaggedChunks = 16;               // chunks per block at most on a ragged batch
+constexpr int kStreamRaggedChunks = 24;               // chunks per block at most on a ragged batch
 constexpr int kSupSplit = 8;                          // PV blocks per head over its support
 constexpr int kStreamUnroll = 8;                      // pages' tiles in flight per row while streaming
 
