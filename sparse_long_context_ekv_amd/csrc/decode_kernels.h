@@ -1029,33 +1029,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
 }
 
-// The row's blocks, combined: weights exp(m_s - max m) in block order.
+// The row's blocks, combined: weights exp(m_s - max m), summed in block
+// order.  One 256-thread block per (b, h): the splits' maxima, weights and
+// sums first (a thread per split), then every channel over the splits in
+// 256 / D interleaved parts (independent loads, several in flight), the
+// parts added in a fixed order.  At most kStreamMaxLists / 4 splits (the
+// plan's row limit).
 template <int D>
-static __global__ __launch_bounds__(D) void softmax_merge_kernel(
+static __global__ __launch_bounds__(256) void softmax_merge_kernel(
     const float* __restrict__ part, int HQ, int nsplit, const float* __restrict__ tau_ref,
     float* __restrict__ out, float* __restrict__ tau_out, int32_t* __restrict__ support_out,
     float* __restrict__ delta_out, int32_t* __restrict__ supref_out) {
-    const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+    constexpr int NP = 256 / D;                       // parts per channel
+    __shared__ float sw[kStreamMaxLists / 4];
+    __shared__ float osum[NP][D];
+    __shared__ float red[4 * 4];                     // block_sum2: two phases of 2 x 4 waves
+    int phase = 0;
+    const int h = blockIdx.x, b = blockIdx.y;
     const size_t oh = (size_t)b * HQ + h;
     const float* pr = part + oh * nsplit * (D + 4);
-    float mm = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; ++s2) mm = fmaxf(mm, pr[(size_t)s2 * (D + 4) + D]);
-    float oo = 0.0f, ll = 0.0f, cc = 0.0f;
-    for (int s2 = 0; s2 < nsplit; ++s2) {
+    const int ns = min(nsplit, kStreamMaxLists / 4);
+    float mx = -INFINITY;
+    for (int s2 = threadIdx.x; s2 < ns; s2 += 256) mx = fmaxf(mx, pr[(size_t)s2 * (D + 4) + D]);
+    mx = block_max<4>(mx, red, phase);
+    float L = 0.0f, C = 0.0f;
+    for (int s2 = threadIdx.x; s2 < ns; s2 += 256) {
         const float* e = pr + (size_t)s2 * (D + 4);
-        const float w = e[D] > -INFINITY ? expf(e[D] - mm) : 0.0f;
-        oo += e[c] * w;
-        ll += e[D + 1] * w;
-        cc += e[D + 2];
+        const float w = e[D] > -INFINITY ? expf(e[D] - mx) : 0.0f;
+        sw[s2] = w;
+        L += e[D + 1] * w;
+        C += e[D + 2];
     }
-    const bool any = cc > 0.0f;
-    out[oh * D + c] = any ? oo / ll : 0.0f;
-    if (c == 0) {
-        tau_out[oh] = any ? mm + logf(ll) : -INFINITY;
-        if (support_out) support_out[oh] = (int32_t)cc;
-        const float tref = tau_ref ? tau_ref[oh] : 0.0f;
-        if (delta_out) delta_out[oh] = any ? 1.0f - ll * expf(mm - tref) : 1.0f;
-        if (supref_out) supref_out[oh] = (int32_t)cc;   // softmax: every token has p > 0
+    block_sum2<4>(L, C, red, phase);                  // barriers: the weights are visible
+    const int c = threadIdx.x % D, pt = threadIdx.x / D;
+    float o = 0.0f;
+#pragma unroll 8
+    for (int s2 = pt; s2 < ns; s2 += NP) o = fmaf(pr[(size_t)s2 * (D + 4) + c], sw[s2], o);
+    osum[pt][c] = o;
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float oo = osum[0][c];
+#pragma unroll
+        for (int k = 1; k < NP; ++k) oo += osum[k][c];
+        const bool any = C > 0.0f;
+        out[oh * D + c] = any ? oo / L : 0.0f;
+        if (c == 0) {
+            tau_out[oh] = any ? mx + logf(L) : -INFINITY;
+            if (support_out) support_out[oh] = (int32_t)C;
+            const float tref = tau_ref ? tau_ref[oh] : 0.0f;
+            if (delta_out) delta_out[oh] = any ? 1.0f - L * expf(mx - tref) : 1.0f;
+            if (supref_out) supref_out[oh] = (int32_t)C;   // softmax: every token has p > 0
+        }
     }
 }
 
@@ -2194,7 +2218,7 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
                 sel_stride, d.B, d.G, d.MP, d.NP, pl.cpb_s, pl.nsplit_s, order, 1.0f / sqrtf((float)D), part);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            softmax_merge_kernel<D><<<dim3(d.HQ, d.B), dim3(D), 0, s>>>(part, d.HQ, pl.nsplit_s, io.tau_ref,
+            softmax_merge_kernel<D><<<dim3(d.HQ, d.B), dim3(256), 0, s>>>(part, d.HQ, pl.nsplit_s, io.tau_ref,
                                                                        io.out, io.tau, io.support, io.delta,
                                                                        io.supref);
             return hipGetLastError();
