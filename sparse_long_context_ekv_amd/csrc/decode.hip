@@ -19,8 +19,11 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
     pl.stream = !pl.fused && alpha > 1.0f;
     const size_t bh = (size_t)d.B * d.HQ;
     // pages per logits block: 64 for the fused path's bf16 keys (8-wave
-    // blocks on the matrix cores), 8 for other selections, 32 over the cache
-    pl.lg_ppb = pl.fused && d.kv_bf16 ? 6 : (sparse ? 3 : 5);
+    // blocks on the matrix cores) where that still gives 256 blocks or more,
+    // 8 for other selections (and for few rows: a small batch's blocks are
+    // latency chains, so more and shorter ones), 32 over the cache
+    const long wide_blocks = (long)d.B * d.G * ((maxp + 63) / 64);
+    pl.lg_ppb = pl.fused && d.kv_bf16 && wide_blocks >= 256 ? 6 : (sparse ? 3 : 5);
     pl.ppb = 1 << pl.lg_ppb;
     pl.nchunk1 = (maxp + pl.ppb - 1) / pl.ppb;
     if (pl.nchunk1 < 1) pl.nchunk1 = 1;

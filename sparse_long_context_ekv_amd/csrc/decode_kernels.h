@@ -2137,15 +2137,19 @@ static hipError_t run_decode(const Dims& d, const DecodePlan& pl, const void* q,
     const int units = d.B * d.G;
     const size_t lds = ((size_t)R * pl.ppb * kPage) * sizeof(float);
     if (pl.fused) {
+        bool wide = false;                                   // 64-page, 8-wave blocks (bf16 keys)
         if constexpr (std::is_same<T, bf16_t>::value) {
-            logits_kernel<T, D, R, false, 8><<<dim3(pl.nchunk1, units), dim3(512), lds, s>>>(
-                (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
-                pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
-        } else {
+            if (pl.lg_ppb == 6) {
+                logits_kernel<T, D, R, false, 8><<<dim3(pl.nchunk1, units), dim3(512), lds, s>>>(
+                    (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
+                    pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
+                wide = true;
+            }
+        }
+        if (!wide)
             logits_kernel<T, D, R, false><<<dim3(pl.nchunk1, units), dim3(256), lds, s>>>(
                 (const T*)q, (const T*)k_cache, pt, sl, sel_pages, sel_count, sel_stride, d.G, d.MP, d.NP,
                 pl.lg_ppb, pl.nslot, pl.nchunk1, 1.0f / sqrtf((float)D), logits, nullptr);
-        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         switch (mode) {
