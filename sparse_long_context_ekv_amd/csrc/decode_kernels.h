@@ -857,20 +857,28 @@ template <int D, int KPW>
 struct VRows {
     static constexpr int VC = D / 64;                 // channels per lane
     uint32_t w[KPW][kPage];                           // VC bf16 of each token (low half when VC = 1)
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ v_cache, const int* sh_phys, int i, int i0,
-                                         int i1, int G, int g) {
+    // Rows of tokens that are not in the sequence (past its end, on an
+    // unreadable page, past the range: those read page 0) are set to zero
+    // once loaded, so that their zero weights never meet whatever those
+    // slots hold (0 x NaN).
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ v_cache, const int* sh_lp, const int* sh_phys,
+                                         int i, int i0, int i1, int G, int g, int n) {
         const int l = threadIdx.x & 63;
 #pragma unroll
         for (int u = 0; u < KPW; ++u) {
             const int ii = i + 4 * u;
             const int t = ii < i1 ? ii - i0 : 0;
             const int ph = sh_phys[t];
-            const bf16_t* src = v_cache + ((size_t)(ii < i1 && ph >= 0 ? ph : 0) * G + g) * kPage * D + VC * l;
+            const bool ok = ii < i1 && ph >= 0;
+            const int ntok = ok ? n - sh_lp[t] * kPage : 0;       // valid tokens of the page (may exceed 16)
+            const bf16_t* src = v_cache + ((size_t)(ok ? ph : 0) * G + g) * kPage * D + VC * l;
 #pragma unroll
             for (int tk = 0; tk < kPage; ++tk) {
                 if constexpr (VC == 2) w[u][tk] = *reinterpret_cast<const uint32_t*>(src + (size_t)tk * D);
                 else w[u][tk] = (uint32_t)src[(size_t)tk * D];
             }
+#pragma unroll
+            for (int tk = 0; tk < kPage; ++tk) w[u][tk] = tk < ntok ? w[u][tk] : 0u;
         }
     }
     __device__ __forceinline__ float get(int u, int tk, int c) const {
@@ -931,7 +939,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     VRows<D, KPW> vr;
     if (p0 < p1) {
         kp.load(k_cache, sh_lp, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g);
-        vr.load(v_cache, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g);
+        vr.load(v_cache, sh_lp, sh_phys, p0 + wv, p0, min(p1, p0 + SP), G, g, n);
     }
     for (int i0 = p0; i0 < p1; i0 += SP) {                  // block-uniform
         const int i1 = min(p1, i0 + SP);
@@ -991,7 +999,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
             }
         }
         // the next step's value tiles
-        if (i1 < p1) vr.load(v_cache, sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g);
+        if (i1 < p1) vr.load(v_cache, sh_lp + (i1 - p0), sh_phys + (i1 - p0), i1 + wv, i1, min(p1, i1 + SP), G, g, n);
     }
     // the block's four waves -> one (m, l, o, count) per head
     if (l == 0) {

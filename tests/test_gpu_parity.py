@@ -29,6 +29,8 @@ def workload(name):
         return W.make_workload(W.CONFIGS[2].scaled(batch=3), "cuda", seq_lens=[5000, 2053, 37])
     if name == "gauss-ragged":
         return W.make_workload(W.CONFIGS[3].scaled(batch=2), "cuda", seq_lens=[8197, 3001])
+    if name == "tiny-ragged":
+        return W.make_workload(W.CONFIGS[1].scaled(batch=2), "cuda", seq_lens=[1500, 37])
     if name == "with-empty":
         return W.make_workload(W.CONFIGS[2].scaled(batch=3), "cuda", seq_lens=[700, 0, 1601])
     if name == "flat":
@@ -642,6 +644,52 @@ def test_softmax_large_logits():
             assert H.tau_close(float(tau_f[b, h]), full["tau"][h]), (b, h)
             assert H.tau_close(float(tau_s[b, h]), sp["tau"][h]), (b, h)
             assert int(sup_f[b, h]) == n
+
+
+@pytest.mark.parametrize("name", ["llama-ragged", "tiny-ragged"])
+@pytest.mark.parametrize("alpha", [1.0, 1.5, 2.0])
+def test_nan_outside_the_sequences(name, alpha):
+    """Cache slots that belong to no token hold NaN: the unused tail of every
+    sequence's last page and an unreferenced physical page 0 (the page the
+    kernels read in place of one past a range).  Decode over the whole cache
+    and over a selection that includes each last page must not see them
+    (bf16 keys: llama-ragged; fp32 keys: tiny-ragged)."""
+    base = workload(name)
+    c = base.cfg
+    nan = float("nan")
+    kc = torch.full((base.num_phys + 1,) + tuple(base.k_cache.shape[1:]), nan, dtype=base.k_cache.dtype, device="cuda")
+    vc = torch.full_like(kc, nan)
+    kc[1:] = base.k_cache
+    vc[1:] = base.v_cache
+    pt = base.page_table + 1
+    for b, n in enumerate(base.seq_lens_host):
+        M = (n + P - 1) // P
+        if n % P:
+            last = int(pt[b, M - 1])
+            kc[last, :, n % P:] = nan
+            vc[last, :, n % P:] = nan
+    wl = W.Workload(cfg=c, q=base.q, k_cache=kc, v_cache=vc, page_table=pt, seq_lens=base.seq_lens,
+                    seq_lens_host=base.seq_lens_host, max_pages=base.max_pages, num_phys=base.num_phys + 1,
+                    planted={})
+    stride = 48
+    sels = []
+    for b, n in enumerate(base.seq_lens_host):
+        M = (n + P - 1) // P
+        pages = sorted(set(range(min(M, stride - 1))) | ({M - 1} if M else set()))
+        sels.append([np.array(pages, dtype=np.int64) for _ in range(c.num_kv_groups)])
+    sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, stride)
+    out_f, tau_f, _, _, _ = _run_decode(wl, alpha)
+    out_s, tau_s, _, _, _ = _run_decode(wl, alpha, sel, cnt, stride)
+    assert bool(torch.isfinite(out_f).all()) and bool(torch.isfinite(out_s).all())
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(base, b)
+        full = oracle.decode.decode(q, K, V, None, alpha)
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, sels[b], alpha)
+        assert np.abs(H.to_np(out_f[b]) - full["out"]).max() <= H.OUT_ATOL, b
+        assert np.abs(H.to_np(out_s[b]) - sp["out"]).max() <= H.OUT_ATOL, b
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau_f[b, h]), full["tau"][h]), (b, h)
+            assert H.tau_close(float(tau_s[b, h]), sp["tau"][h]), (b, h)
 
 
 def test_bitwise_reproducible():
