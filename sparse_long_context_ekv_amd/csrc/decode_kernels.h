@@ -857,10 +857,12 @@ template <int D, int KPW>
 struct VRows {
     static constexpr int VC = D / 64;                 // channels per lane
     uint32_t w[KPW][kPage];                           // VC bf16 of each token (low half when VC = 1)
-    // Rows of tokens that are not in the sequence (past its end, on an
-    // unreadable page, past the range: those read page 0) are set to zero
-    // once loaded, so that their zero weights never meet whatever those
-    // slots hold (0 x NaN).
+    // Each page is read through a buffer resource (the page's tile as base,
+    // its valid tokens x D x 2 bytes as the range), so rows of tokens that
+    // are not in the sequence (past its end, on an unreadable page, past the
+    // range) come back as zero without being read: their zero weights never
+    // meet whatever those slots hold (0 x NaN), at no cost in instructions.
+    // The page is the same for the whole wave, so the resource is scalar.
     __device__ __forceinline__ void load(const bf16_t* __restrict__ v_cache, const int* sh_lp, const int* sh_phys,
                                          int i, int i0, int i1, int G, int g, int n) {
         const int l = threadIdx.x & 63;
@@ -870,15 +872,17 @@ struct VRows {
             const int t = ii < i1 ? ii - i0 : 0;
             const int ph = sh_phys[t];
             const bool ok = ii < i1 && ph >= 0;
-            const int ntok = ok ? n - sh_lp[t] * kPage : 0;       // valid tokens of the page (may exceed 16)
-            const bf16_t* src = v_cache + ((size_t)(ok ? ph : 0) * G + g) * kPage * D + VC * l;
+            const int ntok = ok ? min(n - sh_lp[t] * kPage, kPage) : 0;
+            const int phs = __builtin_amdgcn_readfirstlane(ok ? ph : 0);
+            const int nbytes = __builtin_amdgcn_readfirstlane(max(ntok, 0)) * D * 2;
+            const bf16_t* base = v_cache + ((size_t)phs * G + g) * kPage * D;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferRsrcWord3);
 #pragma unroll
             for (int tk = 0; tk < kPage; ++tk) {
-                if constexpr (VC == 2) w[u][tk] = *reinterpret_cast<const uint32_t*>(src + (size_t)tk * D);
-                else w[u][tk] = (uint32_t)src[(size_t)tk * D];
+                if constexpr (VC == 2) w[u][tk] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * l + tk * D * 2, 0, 0);
+                else w[u][tk] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * l + tk * D * 2, 0, 0);
             }
-#pragma unroll
-            for (int tk = 0; tk < kPage; ++tk) w[u][tk] = tk < ntok ? w[u][tk] : 0u;
         }
     }
     __device__ __forceinline__ float get(int u, int tk, int c) const {
