@@ -853,6 +853,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 // The block's four waves combine (m, l, o) by rescaling to the larger max;
 // softmax_merge_kernel combines the blocks of a row the same way:
 // out = o / l, tau = m + log l.
+// Word 3 of a raw buffer resource on CDNA (32-bit data format, stride 0):
+// with it, a buffer load whose byte offset is at or past the resource's
+// range returns zero and reads nothing.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 template <int D, int KPW>
 struct VRows {
     static constexpr int VC = D / 64;                 // channels per lane

@@ -26,10 +26,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));     // a 16x16 MFMA a
 
 constexpr int kPage = 16;     // tokens per page (the only page size built)
 constexpr int kRow = 16;      // lanes per DPP row
-// Word 3 of a raw buffer resource on CDNA (32-bit data format, stride 0):
-// with it, a buffer load whose byte offset is at or past the resource's
-// range returns zero and reads nothing.
-constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // ---------------------------------------------------------------- loads ----
 // CH channels of element type T as 32-bit words.
