@@ -53,6 +53,9 @@ DecodePlan plan_decode(const Dims& d, int sparse, int sel_stride, float alpha) {
         pl.nsplit_s = (int)((nchunk + cpb - 1) / cpb);
         // rows past kStreamMaxLists / 4 * kStreamMaxChunks chunks (16M tokens) are not built
         pl.too_long = 4L * pl.nsplit_s > kStreamMaxLists;
+    } else if (!pl.fused) {
+        // the same row limit on the softmax path of fp32 keys
+        pl.too_long = (long)maxp > (long)(kStreamMaxLists / 4) * kStreamMaxChunks * kStreamPpb;
     }
     if (pl.fused) {
         // selected logits [B][HQ][nslot]

@@ -137,9 +137,14 @@ int main() {
         const ekv_shape s = shape(1, 32, 8, 128, 1 << 21, 1 << 21, EKV_BF16, EKV_F32);
         size_t n = 0;
         CHECK(decode_query(s, false, 0, 1.5f, &n) == EKV_ERR_UNSUPPORTED, "2M-page full-cache row");
+        CHECK(decode_query(s, false, 0, 1.0f, &n) == EKV_ERR_UNSUPPORTED, "2M-page full-cache softmax row");
+        const ekv_shape sf = shape(1, 32, 8, 128, 1 << 21, 1 << 21, EKV_F32, EKV_F32);
+        CHECK(decode_query(sf, false, 0, 1.0f, &n) == EKV_ERR_UNSUPPORTED, "2M-page fp32 softmax row");
+        CHECK(decode_query(sf, false, 0, 1.5f, &n) == EKV_ERR_UNSUPPORTED, "2M-page fp32 entmax row");
         // the longest supported row, in a ragged batch (the cache holds far fewer pages than B rows of it)
         const ekv_shape r = shape(4, 32, 8, 128, 1 << 20, 1 << 18, EKV_BF16, EKV_F32);
         CHECK(decode_query(r, false, 0, 1.5f, &n) == EKV_OK && n > 0, "1M-page row in a ragged batch");
+        CHECK(decode_query(r, false, 0, 1.0f, &n) == EKV_OK && n > 0, "1M-page softmax row in a ragged batch");
     }
 
     // selection workspace plans
