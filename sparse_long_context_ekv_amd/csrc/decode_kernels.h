@@ -16,9 +16,12 @@
 //   kept; cand_stream_mfma_kernel (bf16 keys) or cand_stream_kernel ->
 //   stream_tau_kernel -> support_pv_kernel -> reduce_kernel (see "streamed
 //   entmax" below).
-//  softmax (alpha = 1): logits_kernel with per-chunk (max, sum exp(s - max),
-//   count) -> softmax_tau_kernel (log-partition) -> pv_kernel (every slot,
-//   p = exp(s - tau)) -> reduce_kernel (fixed-order sum of chunk partials).
+//  softmax (alpha = 1): bf16 keys in one pass, softmax_stream_kernel (keys
+//   and values read once; running max and max-shifted sums per block) ->
+//   softmax_merge_kernel; fp32 keys: logits_kernel with per-chunk (max,
+//   sum exp(s - max), count) -> softmax_tau_kernel (log-partition) ->
+//   pv_kernel (every slot, p = exp(s - tau)) -> reduce_kernel (fixed-order
+//   sum of chunk partials).
 // Bitwise reproducible: the one atomic (the bf16 candidate stream's running
 // max, shared by a block's waves in LDS) only decides which extra entries
 // below the final filter its lists hold, and the threshold kernel orders the
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 // --------------------------------------------- one-pass softmax (bf16) ----
 // alpha = 1 over bf16 keys (full cache or a selection): keys and values are
 // read once.  The streamed path's blocks (ranges of one (b, g), longest
-// sequences first); every wave takes its own pages, 4 per step: logits on
+// sequences first); every wave takes its own pages, 4 per step (2 at r = 8): logits on
 // the matrix cores, then per head a running max m, a running sum
 // l = sum exp(s - m) and o = sum exp(s - m) v over the wave's tokens, both
 // rescaled by exp(m_old - m_new) when m grows (the max-shifted sums of the
@@ -853,6 +856,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 // The block's four waves combine (m, l, o) by rescaling to the larger max;
 // softmax_merge_kernel combines the blocks of a row the same way:
 // out = o / l, tau = m + log l.
+
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, stride 0):
 // with it, a buffer load whose byte offset is at or past the resource's
 // range returns zero and reads nothing.
