@@ -80,6 +80,22 @@ def test_noalloc_decode_matches_workspace_decode(alpha):
                 assert H.tau_close(float(t1[b, h]), sp["tau"][h])
 
 
+def test_noalloc_full_cache_softmax():
+    """Full-cache softmax on the static scratch (bf16 keys: the one-pass path;
+    fp32 keys: the logits path), second call smaller than the first, equal
+    bit for bit to the decode with a workspace."""
+    wl = W.make_workload(W.CONFIGS[2].scaled(batch=2), "cuda", seq_lens=[9000, 1234])
+    small = W.make_workload(W.CONFIGS[1], "cuda")
+    for name, w in (("softmax, full cache, 2 sequences", wl), ("softmax, full cache, tiny", small)):
+        print(f"[case] noalloc {name}", flush=True)
+        (o1, t1, s1), (o2, t2, s2) = _both(w, 1.0, None, None, 0)
+        assert torch.equal(o1, o2) and torch.equal(t1, t2) and torch.equal(s1, s2)
+        for b in range(w.cfg.batch):
+            q, K, V, n = H.seq_logical(w, b)
+            ref = oracle.decode.decode(q, K, V, None, 1.0)
+            assert np.abs(H.to_np(o1[b]) - ref["out"]).max() <= H.OUT_ATOL
+
+
 def test_noalloc_full_cache_decode_and_oversize_rejection():
     """Full-cache decode on the static scratch (second call smaller than the
     first), and a decode larger than the scratch turned away with
