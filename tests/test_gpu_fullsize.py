@@ -192,7 +192,31 @@ def test_extreme_1m_topk_and_full_cache():
         assert np.abs(H.to_np(full.out[b, h]) - o).max() <= H.OUT_ATOL
         assert abs(int(full.support[b, h]) - k) <= int(np.count_nonzero(
             np.abs(0.5 * s[h] - tau_full) < 1e-5 * max(1.0, abs(tau_full))))
-    del s, dec, full, wl
+    # full-cache softmax (the one-pass path, as the bench times it): the
+    # log-partition of every head, and the output of four heads in four
+    # groups, over all 1,048,576 tokens (values read in 128K-token chunks)
+    print(f"[case] {cfg.name} softmax", flush=True)
+    sm = ekv.FullDecoder(wl, 1.0)
+    sm.run()
+    H.sync()
+    heads = (0, 9, 18, 31)
+    pw = {}
+    for h in range(HQ):
+        p, lse, _ = oracle.entmax.entmax(s[h], 1.0)
+        assert H.tau_close(float(sm.tau[b, h]), lse), (h, float(sm.tau[b, h]), lse)
+        if h in heads:
+            pw[h] = p
+    acc = {h: np.zeros(cfg.head_dim) for h in heads}
+    for t0 in range(0, n, 1 << 17):
+        t1 = min(n, t0 + (1 << 17))
+        V = H.seq_tokens_f64(wl.v_cache, wl, b, np.arange(t0, t1))
+        for h in heads:
+            acc[h] += pw[h][t0:t1] @ V[:, h // r, :]
+        del V
+    for h in heads:
+        assert np.abs(H.to_np(sm.out[b, h]) - acc[h]).max() <= H.OUT_ATOL, h
+    assert bool((sm.support[b] == n).all())
+    del s, dec, full, sm, wl
 
 
 @functools.lru_cache(maxsize=1)
