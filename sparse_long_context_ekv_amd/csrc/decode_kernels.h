@@ -777,7 +777,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         kp.template contract<R>(mq, acc);
         bool full = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) full |= scnt[j] > CB - KPW * kPage;
+        // rows of lanes that hold heads only: the other rows' counts follow
+        // row 0's but a flush never resets them
+        for (int j = 0; j < 4; ++j) full |= hq < NR && scnt[j] > CB - KPW * kPage;
         if (__ballot(full)) flush(false);                    // wave-uniform
         bool live[KPW];
 #pragma unroll
