@@ -232,8 +232,11 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  *   out = 0, tau = -inf, support = 0, delta = 1, support_ref = 0.
  * Rows of more than 2^20 pages (16M tokens: max_pages_per_seq for
  *   sel_pages == NULL, else sel_stride) return EKV_ERR_UNSUPPORTED.
- * Needs a workspace (see conventions); its size depends on sel_pages being
- * NULL or not and on sel_stride.                                           */
+ * Cache slots that hold no token of a sequence (the tail of its last page,
+ *   pages no table entry names) may hold any bits, NaN included: no output
+ *   depends on them.
+ * Needs a workspace (see conventions); its size depends on the shape, on
+ * alpha (1 or not), on sel_pages being NULL or not and on sel_stride.      */
 ekv_status ekv_entmax_decode(const ekv_shape* shape, const void* q,
                              const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens,
