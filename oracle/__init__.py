@@ -11,7 +11,7 @@ Entmax Attention" (Duarte, Couceiro, Treviso; arXiv 2605.21649), abbreviated
 [EKV] below, plus the GQA notation of "EntroPrefill: Renyi-Guided Context
 Pruning" section 2.1 Eq. (1) for the head-to-group map.  Each function cites
 the section, equation or appendix it follows.  Where the page text is damaged
-or silent, the reading taken is named (R1..R14) and listed in the design doc.
+or silent, the reading taken is named (R1..R14) at the function that takes it.
 
 Everything is numpy/scipy in float64.  Inputs stored in bf16 or fp32 are
 up-cast exactly before any arithmetic.
