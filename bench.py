@@ -293,7 +293,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only (the decode path is not sharded); "
+        print(json.dumps({"error": "the library runs on one GPU only (the decode path is not sharded); "
                                    "--gpus must be 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
