@@ -212,7 +212,9 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  *   form on the support found.
  * sel_pages == NULL selects every page (full-cache decode); otherwise
  *   sel_pages [B][G][sel_stride] logical page indices (ascending not
- *   required) and sel_count [B][G] of them are used.
+ *   required) and sel_count [B][G] of them are used.  An index outside
+ *   [0, pages of the sequence), or a page whose table entry lies outside
+ *   [0, num_phys_pages), contributes no token.
  * tau_hint [B][HQ] fp32 (NULL ok; alpha > 1): a start for the threshold
  *   iteration, in x units -- the selection's threshold estimate, which
  *   [EKV] section 4.4 hands to decode with the selected pages (ekv_select's

@@ -692,6 +692,43 @@ def test_nan_outside_the_sequences(name, alpha):
             assert H.tau_close(float(tau_s[b, h]), sp["tau"][h]), (b, h)
 
 
+@pytest.mark.parametrize("name,alpha,budget", [("llama-ragged", 1.0, 40), ("llama-ragged", 1.5, 40),
+                                               ("llama-ragged", 2.0, 300), ("llama-ragged", 1.0, 300),
+                                               ("tiny-ragged", 1.0, 40), ("tiny-ragged", 1.5, 40)])
+def test_decode_skips_invalid_selected_pages(name, alpha, budget):
+    """Selections that name pages outside the sequence (-1, the page count,
+    beyond it) and a selected page whose table entry lies outside the cache:
+    those contribute no token; the rest decode as the oracle does on the valid
+    pages (fused and one-pass paths at 40 pages, the streamed paths at 300)."""
+    base = workload(name)
+    c = base.cfg
+    stride = budget + 3
+    pt = base.page_table.clone()
+    sels, bad = [], None
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(base, b)
+        sels.append(oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", alpha, budget)["sel"])
+    bad = int(sels[0][0][0])                              # page of sequence 0 with an unreadable table entry
+    pt[0, bad] = -5
+    wl = W.Workload(cfg=c, q=base.q, k_cache=base.k_cache, v_cache=base.v_cache, page_table=pt,
+                    seq_lens=base.seq_lens, seq_lens_host=base.seq_lens_host, max_pages=base.max_pages,
+                    num_phys=base.num_phys, planted={})
+    given, valid = [], []
+    for b in range(c.batch):
+        M = (base.seq_lens_host[b] + P - 1) // P
+        given.append([np.concatenate([sg, np.array([-1, M, M + 7], dtype=np.int64)]) for sg in sels[b]])
+        valid.append([sg[sg != bad] if b == 0 else sg for sg in sels[b]])
+    sel, cnt = _oracle_sel_tensor(given, c.batch, c.num_kv_groups, stride)
+    out, tau, sup, _, _ = _run_decode(wl, alpha, sel, cnt, stride)
+    assert bool(torch.isfinite(out).all())
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(base, b)
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, valid[b], alpha)
+        assert np.abs(H.to_np(out[b]) - sp["out"]).max() <= H.OUT_ATOL, b
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau[b, h]), sp["tau"][h]), (b, h)
+
+
 def test_bitwise_reproducible():
     wl = workload("llama-ragged")
     dec = ekv.Decoder(wl, "topk", 1.5, wl.cfg.budget_pages)
