@@ -214,7 +214,8 @@ ekv_status ekv_select(const ekv_shape* shape, int32_t selector, const int32_t* s
  *   sel_pages [B][G][sel_stride] logical page indices (ascending not
  *   required) and sel_count [B][G] of them are used.  An index outside
  *   [0, pages of the sequence), or a page whose table entry lies outside
- *   [0, num_phys_pages), contributes no token.
+ *   [0, num_phys_pages), contributes no token; a page named twice
+ *   contributes its tokens twice (ekv_select never names one twice).
  * tau_hint [B][HQ] fp32 (NULL ok; alpha > 1): a start for the threshold
  *   iteration, in x units -- the selection's threshold estimate, which
  *   [EKV] section 4.4 hands to decode with the selected pages (ekv_select's
