@@ -729,6 +729,29 @@ def test_decode_skips_invalid_selected_pages(name, alpha, budget):
             assert H.tau_close(float(tau[b, h]), sp["tau"][h]), (b, h)
 
 
+@pytest.mark.parametrize("alpha,budget", [(1.0, 40), (1.5, 40), (2.0, 300)])
+def test_decode_page_named_twice(alpha, budget):
+    """A selection that names a page twice decodes over its tokens twice, as
+    the oracle does over the same page list (fused or one-pass at 40 pages,
+    streamed at 300)."""
+    wl = workload("llama-ragged")
+    c = wl.cfg
+    stride = budget + 3
+    sels = []
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sg = oracle.decode.select_pages(q, K, n, P, c.num_kv_groups, "topk", alpha, budget)["sel"]
+        sels.append([np.concatenate([x, x[:3]]) for x in sg])
+    sel, cnt = _oracle_sel_tensor(sels, c.batch, c.num_kv_groups, stride)
+    out, tau, _, _, _ = _run_decode(wl, alpha, sel, cnt, stride)
+    for b in range(c.batch):
+        q, K, V, n = H.seq_logical(wl, b)
+        sp = oracle.decode.sparse_decode_groups(q, K, V, n, P, sels[b], alpha)
+        assert np.abs(H.to_np(out[b]) - sp["out"]).max() <= H.OUT_ATOL, b
+        for h in range(c.num_q_heads):
+            assert H.tau_close(float(tau[b, h]), sp["tau"][h]), (b, h)
+
+
 def test_bitwise_reproducible():
     wl = workload("llama-ragged")
     dec = ekv.Decoder(wl, "topk", 1.5, wl.cfg.budget_pages)
